@@ -1,0 +1,401 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+The DiTango pages (gist.science 2607.15650, "Methodology §2, State Composition") state
+that attention states (output, log-sum-exp) of KV partitions compose associatively and
+commutatively and that the composition replaces attention over the raw K/V.  The pages
+print no worked example, so the oracle is pinned to:
+
+* softmax attention over all keys computed by brute force (scalar loops, no partitions),
+* closed forms (q = 0, constant V, identical keys),
+* algebraic invariants (associativity, commutativity, weights summing to 1),
+* the selective step's closed form with a stale cache,
+* bfloat16 rounding of known bit patterns and RoPE's rotation properties.
+
+`test_pins_catch_planted_mistakes` plants plausible mistakes in copies of the oracle's
+functions and checks that the pins reject each of them.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as OA
+import workloads as W
+
+
+def brute_attention(q, k, v, scale):
+    """Softmax attention by scalar loops: q [n,H,D], k,v [m,H,D] -> O [n,H,D], lse [H,n]."""
+    n, H, D = q.shape
+    m = k.shape[0]
+    O = np.zeros((n, H, D))
+    lse = np.zeros((H, n))
+    for h in range(H):
+        for r in range(n):
+            s = [scale * sum(q[r, h, d] * k[j, h, d] for d in range(D)) for j in range(m)]
+            mx = max(s)
+            z = sum(math.exp(x - mx) for x in s)
+            lse[h, r] = mx + math.log(z)
+            for d in range(D):
+                O[r, h, d] = sum(math.exp(s[j] - mx) / z * v[j, h, d] for j in range(m))
+    return O, lse
+
+
+def rand_qkv(rng, n, m, H, D):
+    return (rng.standard_normal((n, H, D)), rng.standard_normal((m, H, D)), rng.standard_normal((m, H, D)))
+
+
+def states_of(q, k, v, offs, scale, partition_state=OA.partition_state):
+    Os, ls = [], []
+    for p in range(len(offs) - 1):
+        O, l = partition_state(q, k[offs[p]:offs[p + 1]], v[offs[p]:offs[p + 1]], scale)
+        Os.append(O)
+        ls.append(l)
+    return Os, ls
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_merge_equals_full(partition_state=OA.partition_state, merge=OA.merge_states, seed=0):
+    """Max error of merge(all partition states) vs brute-force full attention."""
+    rng = np.random.default_rng(seed)
+    q, k, v = rand_qkv(rng, 7, 29, 2, 8)
+    q *= 1.7  # spread the scores so that partitions carry very different weight
+    scale = 1 / math.sqrt(8)
+    offs = [0, 5, 5, 13, 29]            # includes an empty partition
+    Os, ls = states_of(q, k, v, offs, scale, partition_state)
+    O, lse = merge(Os, ls)
+    Ob, lb = brute_attention(q, k, v, scale)
+    return max(np.abs(O - Ob).max(), np.abs(lse - lb).max())
+
+
+def pin_single_partition(partition_state=OA.partition_state, seed=1):
+    rng = np.random.default_rng(seed)
+    q, k, v = rand_qkv(rng, 5, 17, 3, 4)
+    scale = 0.37
+    O, lse = partition_state(q, k, v, scale)
+    Ob, lb = brute_attention(q, k, v, scale)
+    return max(np.abs(O - Ob).max(), np.abs(lse - lb).max())
+
+
+def pin_q_zero_closed_form(partition_state=OA.partition_state, merge=OA.merge_states, seed=2):
+    """q = 0: every score is 0, so lse_p = ln|p|, O_p = mean(V_p), merged O = mean(V),
+    merge weight of p = |p| / S."""
+    rng = np.random.default_rng(seed)
+    _, k, v = rand_qkv(rng, 1, 23, 2, 6)
+    q = np.zeros((4, 2, 6))
+    offs = [0, 3, 11, 23]
+    Os, ls = states_of(q, k, v, offs, 0.5, partition_state)
+    err = 0.0
+    for p in range(3):
+        a, b = offs[p], offs[p + 1]
+        err = max(err, np.abs(ls[p] - math.log(b - a)).max())
+        err = max(err, np.abs(Os[p] - v[a:b].mean(axis=0)[None]).max())
+    O, lse = merge(Os, ls)
+    err = max(err, np.abs(O - v.mean(axis=0)[None]).max(), np.abs(lse - math.log(23)).max())
+    Wt = OA.merge_weights(ls, lse)
+    for p in range(3):
+        err = max(err, np.abs(Wt[p] - (offs[p + 1] - offs[p]) / 23).max())
+    return err
+
+
+def pin_equal_keys(partition_state=OA.partition_state, seed=3):
+    """All keys equal to k0: lse = scale q.k0 + ln m and O = mean(V)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((3, 2, 5))
+    k0 = rng.standard_normal((1, 2, 5))
+    k = np.repeat(k0, 9, axis=0)
+    v = rng.standard_normal((9, 2, 5))
+    O, lse = partition_state(q, k, v, 0.8)
+    want_lse = 0.8 * np.einsum("nhd,hd->hn", q, k0[0]) + math.log(9)
+    return max(np.abs(lse - want_lse).max(), np.abs(O - v.mean(axis=0)[None]).max())
+
+
+def pin_constant_v(partition_state=OA.partition_state, merge=OA.merge_states, seed=4):
+    """V identically c: every partition state and the merge equal c (softmax rows sum to 1)."""
+    rng = np.random.default_rng(seed)
+    q, k, _ = rand_qkv(rng, 6, 20, 2, 3)
+    c = np.array([0.25, -1.5, 3.0])
+    v = np.broadcast_to(c, (20, 2, 3)).copy()
+    Os, ls = states_of(q * 3, k, v, [0, 4, 12, 20], 0.9, partition_state)
+    O, _ = merge(Os, ls)
+    return max([np.abs(x - c).max() for x in Os] + [np.abs(O - c).max()])
+
+
+def pin_assoc_comm(merge=OA.merge_states, seed=5):
+    rng = np.random.default_rng(seed)
+    Os = [rng.standard_normal((4, 2, 3)) for _ in range(3)]
+    ls = [rng.standard_normal((2, 4)) * 3 for _ in range(3)]
+    ab = merge(Os[:2], ls[:2])
+    abc1 = merge([ab[0], Os[2]], [ab[1], ls[2]])
+    bc = merge(Os[1:], ls[1:])
+    abc2 = merge([Os[0], bc[0]], [ls[0], bc[1]])
+    err = max(np.abs(abc1[0] - abc2[0]).max(), np.abs(abc1[1] - abc2[1]).max())
+    for perm in itertools.permutations(range(3)):
+        r = merge([Os[i] for i in perm], [ls[i] for i in perm])
+        err = max(err, np.abs(r[0] - abc1[0]).max(), np.abs(r[1] - abc1[1]).max())
+    return err
+
+
+ALL_PINS = [pin_merge_equals_full, pin_single_partition, pin_q_zero_closed_form, pin_equal_keys,
+            pin_constant_v, pin_assoc_comm]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    assert pin() < 1e-12
+
+
+def test_merge_weights_sum_to_one():
+    rng = np.random.default_rng(6)
+    q, k, v = rand_qkv(rng, 9, 40, 2, 8)
+    Os, ls = states_of(q * 2, k, v, [0, 1, 10, 10, 33, 40], 0.35)
+    O, lse = OA.merge_states(Os, ls)
+    Wt = OA.merge_weights(ls, lse)
+    assert np.abs(Wt.sum(axis=0) - 1).max() < 1e-12
+    assert (Wt[2] == 0).all()  # the empty partition carries no weight
+
+
+def test_all_empty_merge():
+    O, lse = OA.merge_states([np.zeros((2, 1, 3))] * 2, [np.full((1, 2), -np.inf)] * 2)
+    assert (O == 0).all() and np.isneginf(lse).all()
+
+
+def test_pins_catch_planted_mistakes():
+    """Each planted mistake must make at least one pin fail (error > 1e-6)."""
+
+    def ps_no_scale(q, k, v, scale):
+        return OA.partition_state(q, k, v, 1.0)
+
+    def ps_kv_swapped(q, k, v, scale):
+        return OA.partition_state(q, v, k, scale)
+
+    def ps_drop_max(q, k, v, scale):
+        O, lse = OA.partition_state(q, k, v, scale)
+        return O, lse - np.log(max(k.shape[0], 1))  # drops the ln(sum) normaliser's count
+
+    def ps_off_by_one(q, k, v, scale):
+        if k.shape[0] > 1:
+            return OA.partition_state(q, k[1:], v[1:], scale)
+        return OA.partition_state(q, k, v, scale)
+
+    def ps_head_mixup(q, k, v, scale):
+        return OA.partition_state(q, k[:, ::-1], v, scale)
+
+    def merge_wrong_sign(Os, ls):
+        O, lse = OA.merge_states(Os, [-x for x in ls])
+        return O, -lse
+
+    def merge_unweighted(Os, ls):
+        O, lse = OA.merge_states(Os, ls)
+        return sum(Os) / len(Os), lse
+
+    def merge_drop_last(Os, ls):
+        return OA.merge_states(Os[:-1], ls[:-1]) if len(Os) > 1 else OA.merge_states(Os, ls)
+
+    def merge_first_wins(Os, ls):
+        O, lse = OA.merge_states(Os, ls)
+        return O, np.max(np.stack(ls), axis=0)
+
+    mutants_ps = [ps_no_scale, ps_kv_swapped, ps_drop_max, ps_off_by_one, ps_head_mixup]
+    mutants_merge = [merge_wrong_sign, merge_unweighted, merge_drop_last, merge_first_wins]
+    for m in mutants_ps:
+        errs = [pin_merge_equals_full(partition_state=m), pin_single_partition(partition_state=m),
+                pin_q_zero_closed_form(partition_state=m), pin_equal_keys(partition_state=m),
+                pin_constant_v(partition_state=m)]
+        assert max(errs) > 1e-6, m.__name__
+    for m in mutants_merge:
+        errs = [pin_merge_equals_full(merge=m), pin_q_zero_closed_form(merge=m),
+                pin_constant_v(merge=m), pin_assoc_comm(merge=m)]
+        assert max(errs) > 1e-6, m.__name__
+
+
+# ----------------------------------------------------------------------------- selective step
+
+def _offs_blocks():
+    return [0, 6, 11], [0, 4, 9, 9, 15, 22]   # 2 query blocks, 5 partitions (one empty)
+
+
+def test_selective_step_closed_form_stale_cache():
+    """q = 0 makes every merge weight |p| / S in both steps.  With V = c now and V = c'
+    when the cache was filled, the output is (sum_fresh |p| c + sum_reused |p| c') / S."""
+    qo, ko = _offs_blocks()
+    H, D, S = 2, 3, ko[-1]
+    rows = np.arange(qo[-1])
+    rng = np.random.default_rng(7)
+    k = rng.standard_normal((S, H, D))
+    c_old, c_new = np.array([1.0, 2.0, -3.0]), np.array([-0.5, 0.25, 4.0])
+    q = np.zeros((len(rows), H, D))
+    cache = OA.StateCache.empty(rows, 5, H, D, 2)
+    full = np.ones((2, 5), dtype=np.uint8)
+    OA.selective_step(q, k, np.broadcast_to(c_old, (S, H, D)).copy(), rows, qo, ko, full, cache, 0.3)
+    mask = np.array([[1, 0, 1, 0, 1], [0, 1, 1, 0, 0]], dtype=np.uint8)
+    res = OA.selective_step(q, k, np.broadcast_to(c_new, (S, H, D)).copy(), rows, qo, ko, mask, cache, 0.3)
+    sizes = np.diff(ko)
+    for i in range(2):
+        fresh = sum(sizes[p] for p in range(5) if mask[i, p])
+        want = (fresh * c_new + (S - fresh) * c_old) / S
+        sel = slice(qo[i], qo[i + 1])
+        assert np.abs(res.O[sel] - want).max() < 1e-12
+    assert np.abs(res.lse - math.log(S)).max() < 1e-12
+
+
+def test_selective_all_recompute_is_anchor_and_full_attention():
+    qo, ko = _offs_blocks()
+    rng = np.random.default_rng(8)
+    q, k, v = rand_qkv(rng, qo[-1], ko[-1], 2, 4)
+    rows = np.arange(qo[-1])
+    cache = OA.StateCache.empty(rows, 5, 2, 4, 2)
+    res = OA.selective_step(q, k, v, rows, qo, ko, np.ones((2, 5), np.uint8), cache, 0.5)
+    Os, ls = states_of(q, k, v, ko, 0.5)
+    O, lse = OA.merge_states(Os, ls)
+    assert np.array_equal(res.O, O) and np.array_equal(res.lse, lse)
+    Ob, lb = brute_attention(q, k, v, 0.5)
+    assert np.abs(res.O - Ob).max() < 1e-12 and np.abs(res.lse - lb).max() < 1e-12
+
+
+def test_selective_reuse_of_unchanged_inputs_is_full_attention():
+    qo, ko = _offs_blocks()
+    rng = np.random.default_rng(9)
+    q, k, v = rand_qkv(rng, qo[-1], ko[-1], 2, 4)
+    rows = np.arange(qo[-1])
+    cache = OA.StateCache.empty(rows, 5, 2, 4, 2)
+    OA.selective_step(q, k, v, rows, qo, ko, np.ones((2, 5), np.uint8), cache, 0.5)
+    mask = np.array([[1, 0, 0, 0, 0], [0, 0, 0, 1, 0]], np.uint8)
+    res = OA.selective_step(q, k, v, rows, qo, ko, mask, cache, 0.5)
+    Ob, lb = brute_attention(q, k, v, 0.5)
+    assert np.abs(res.O - Ob).max() < 1e-12 and np.abs(res.lse - lb).max() < 1e-12
+
+
+def test_selective_step_rejects_invalid_reuse():
+    qo, ko = _offs_blocks()
+    rows = np.arange(qo[-1])
+    cache = OA.StateCache.empty(rows, 5, 1, 2, 2)
+    with pytest.raises(ValueError):
+        OA.selective_step(np.zeros((11, 1, 2)), np.zeros((22, 1, 2)), np.zeros((22, 1, 2)), rows,
+                          qo, ko, np.array([[1, 1, 1, 1, 1], [1, 0, 1, 1, 1]], np.uint8), cache, 1.0)
+
+
+def test_selective_step_on_row_sample_matches_all_rows():
+    """Each output row depends only on its own query, so a row sample gives the same rows."""
+    qo, ko = _offs_blocks()
+    rng = np.random.default_rng(10)
+    q, k, v = rand_qkv(rng, qo[-1], ko[-1], 2, 4)
+    rows = np.arange(qo[-1])
+    mask = np.array([[1, 1, 1, 0, 1], [1, 1, 1, 1, 1]], np.uint8)
+    c1 = OA.StateCache.empty(rows, 5, 2, 4, 2)
+    c1.valid[:] = True
+    r1 = OA.selective_step(q, k, v, rows, qo, ko, mask, c1, 0.5)
+    sub = np.array([0, 3, 7, 10])
+    c2 = OA.StateCache.empty(sub, 5, 2, 4, 2)
+    c2.valid[:] = True
+    r2 = OA.selective_step(q[sub], k, v, sub, qo, ko, mask, c2, 0.5)
+    assert np.array_equal(r1.O[sub], r2.O) and np.array_equal(r1.lse[:, sub], r2.lse)
+
+
+# ----------------------------------------------------------------------------- importance, delta
+
+def test_importance_q_zero_closed_form():
+    qo, ko = _offs_blocks()
+    rng = np.random.default_rng(11)
+    _, k, v = rand_qkv(rng, 1, ko[-1], 2, 4)
+    rows = np.arange(qo[-1])
+    q = np.zeros((len(rows), 2, 4))
+    cache = OA.StateCache.empty(rows, 5, 2, 4, 2)
+    res = OA.selective_step(q, k, v, rows, qo, ko, np.ones((2, 5), np.uint8), cache, 0.5)
+    w = OA.importance(res.weights, rows, qo)
+    want = np.diff(ko) / ko[-1]
+    assert np.abs(w - want[None]).max() < 1e-12
+    assert np.abs(w.sum(axis=1) - 1).max() < 1e-12
+
+
+def test_importance_concentrates_on_the_aligned_partition():
+    """Keys of partition 2 equal to a large multiple of the query: its weight dominates."""
+    rng = np.random.default_rng(12)
+    qv = rng.standard_normal((1, 1, 8))
+    q = np.repeat(qv, 3, axis=0)
+    k = rng.standard_normal((20, 1, 8)) * 0.1
+    k[10:15] = qv * 10
+    v = rng.standard_normal((20, 1, 8))
+    ko = [0, 5, 10, 15, 20]
+    rows = np.arange(3)
+    cache = OA.StateCache.empty(rows, 4, 1, 8, 1)
+    res = OA.selective_step(q, k, v, rows, [0, 3], ko, np.ones((1, 4), np.uint8), cache, 1.0)
+    w = OA.importance(res.weights, rows, [0, 3])
+    assert w[0, 2] > 0.999 and abs(w.sum() - 1) < 1e-12
+
+
+@pytest.mark.parametrize("c", [1.0, 1.03, 0.5, -2.0])
+def test_local_change_scaled_v(c):
+    """Q, K fixed and V_t = c V_{t-1}: every partition state scales by c, so delta = |c - 1|."""
+    qo, ko = _offs_blocks()
+    rng = np.random.default_rng(13)
+    q, k, v = rand_qkv(rng, qo[-1], ko[-1], 2, 4)
+    rows = np.arange(qo[-1])
+    local = [0, 3]
+    cache = OA.StateCache.empty(rows, 5, 2, 4, 2)
+    OA.selective_step(q, k, v, rows, qo, ko, np.ones((2, 5), np.uint8), cache, 0.5)
+    old = np.stack([cache.exact_O[local[i], r] for r, i in zip(rows, OA.block_of_rows(rows, qo))])
+    OA.selective_step(q, k, c * v, rows, qo, ko, np.ones((2, 5), np.uint8), cache, 0.5)
+    new = np.stack([cache.exact_O[local[i], r] for r, i in zip(rows, OA.block_of_rows(rows, qo))])
+    d = OA.local_change(new, old, rows, qo)
+    assert np.abs(d - abs(c - 1)).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------- rounding
+
+def test_bf16_rounding_known_patterns():
+    vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -2.5, 3.0e38, 2 ** -130])
+    want = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x7F62, 0x0008]  # 2^-130 = 8 * 2^-133 (subnormal)
+    got = W.f32_to_bf16_bits(vals.astype(np.float32))
+    assert [int(x) for x in got] == want
+    r = OA.round_bf16(vals)
+    assert np.array_equal(r, W.bf16_bits_to_f32(np.array(want, np.uint16)).astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- RoPE (input prep)
+
+def test_rope_preserves_norm_and_is_relative():
+    rng = np.random.default_rng(14)
+    grid = (5, 6, 7)
+    D = 128
+    ang = W.rope_angles(grid, D, 0, 210)
+    x = rng.standard_normal((210, 1, D))
+    y = W.apply_rope(x, ang)
+    assert np.abs(np.linalg.norm(y, axis=-1) - np.linalg.norm(x, axis=-1)).max() < 1e-12
+    assert np.abs(y[0] - x[0]).max() == 0  # position (0,0,0) is the identity
+    # <R(m) a, R(n) b> depends only on m - n per axis
+    a, b = rng.standard_normal((1, 1, D)), rng.standard_normal((1, 1, D))
+    co = W.token_coords(grid, 0, 210)
+    idx = {tuple(c): i for i, c in enumerate(co)}
+
+    def dot(m, n):
+        ra = W.apply_rope(a, ang[idx[m]][None])
+        rb = W.apply_rope(b, ang[idx[n]][None])
+        return float((ra * rb).sum())
+
+    assert abs(dot((1, 2, 3), (0, 1, 1)) - dot((4, 5, 6), (3, 4, 4))) < 1e-10
+    assert abs(dot((1, 2, 3), (0, 1, 1)) - dot((1, 2, 4), (0, 1, 1))) > 1e-6
+
+
+def test_rope_pair_split():
+    assert W.rope_pairs_per_axis(128, 3) == [22, 21, 21]
+    assert W.rope_pairs_per_axis(128, 2) == [32, 32]
+    assert W.rope_pairs_per_axis(64, 2) == [16, 16]
+
+
+def test_partition_offsets_of_workloads():
+    assert W.workload("video720p").kv_offsets[1] == 4725
+    o = W.workload("share32").kv_offsets
+    assert np.diff(o).tolist() == [2363] * 16 + [2362] * 16
+    o = W.workload("longvideo").kv_offsets
+    assert np.diff(o).tolist() == [4613] * 16 + [4612] * 16
+    assert W.workload("share32").S_q == 2363
+
+
+def test_seeded_draws_are_chunk_consistent():
+    w = W.workload("tiny")
+    full = W.normal_tokens(w.seed, W.T_Q, 0, 5000, 1, 4)
+    part = W.normal_tokens(w.seed, W.T_Q, 1999, 4100, 1, 4)
+    assert np.array_equal(full[1999:4100], part)

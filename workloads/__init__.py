@@ -1,0 +1,366 @@
+"""Seeded synthetic inputs for partitioned DiT self-attention with selective state reuse.
+
+This module is input preparation only, shared by the CPU oracle and the GPU path:
+
+* seeded standard-normal draws for Q, K, V and for the perturbation noises,
+* axial rotary position embedding (RoPE) of Q and K over the latent token grid,
+* rounding to bfloat16 (round to nearest, ties to even),
+* the workload descriptions: token grid, head count and width, partition offsets,
+  query-block offsets, each block's local partition and the group layout.
+
+No step of the attention method (partition states, merging, importance, local change,
+selection) is computed here.
+
+The workloads follow the DiTango pages (gist.science 2607.15650, "Methodology" /
+"방법론"): a DiT runs non-causal attention over the whole spatiotemporal token sequence
+(row-major over (t, h, w)), split into spatially contiguous partitions.  Real model
+activations are not available, so Q, K, V are N(0, 1) draws of the same shapes.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import math
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+# Tokens per independently seeded draw chunk.  Every chunk of every tensor gets its own
+# PCG64 stream, spawned from (seed, tensor id, chunk index), so any subset of tokens can be
+# regenerated without drawing the rest, and chunks can be drawn in parallel threads.
+CHUNK_TOKENS = 2048
+
+# Tensor ids of the seeded streams.
+T_Q, T_K, T_V = 0, 1, 2
+
+
+def noise_id(step: int, which: int) -> int:
+    """Stream id of the perturbation noise applied at `step` (>= 1) to tensor `which`."""
+    return 3 + 3 * (step - 1) + which
+
+
+# --------------------------------------------------------------------------------------
+# bfloat16 helpers (input rounding)
+# --------------------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bit patterns.
+
+    Inputs are finite by construction (normal draws), so NaN/inf handling is not needed."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# --------------------------------------------------------------------------------------
+# Token grid and axial RoPE
+# --------------------------------------------------------------------------------------
+
+def token_coords(grid: Sequence[int], start: int, stop: int) -> np.ndarray:
+    """Coordinates [stop-start, len(grid)] of tokens in row-major order over `grid`."""
+    idx = np.arange(start, stop, dtype=np.int64)
+    coords = np.empty((stop - start, len(grid)), dtype=np.int64)
+    rem = idx
+    for a in range(len(grid) - 1, -1, -1):
+        coords[:, a] = rem % grid[a]
+        rem = rem // grid[a]
+    return coords
+
+
+def rope_pairs_per_axis(D: int, n_axes: int) -> List[int]:
+    """Split the D/2 rotation pairs over the grid axes; the first axis takes the remainder.
+
+    2D with D=128 gives (32, 32); 3D with D=128 gives (22, 21, 21) for (t, h, w)."""
+    npairs = D // 2
+    each = npairs // n_axes
+    counts = [each] * n_axes
+    counts[0] += npairs - each * n_axes
+    return counts
+
+
+def rope_angles(grid: Sequence[int], D: int, start: int, stop: int, base: float = 10000.0) -> np.ndarray:
+    """Rotation angle of every (token, pair): [stop-start, D/2] float64.
+
+    Pair j of axis a (pairs are laid out axis by axis) turns by coord_a * base**(-j/n_a)."""
+    coords = token_coords(grid, start, stop).astype(np.float64)
+    counts = rope_pairs_per_axis(D, len(grid))
+    cols = []
+    for a, n_a in enumerate(counts):
+        theta = base ** (-np.arange(n_a, dtype=np.float64) / n_a)
+        cols.append(coords[:, a:a + 1] * theta[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def apply_rope(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
+    """Rotate interleaved pairs (2j, 2j+1) of x [n, H, D] by angles [n, D/2]; float64 result."""
+    x = x.astype(np.float64, copy=False)
+    c = np.cos(angles)[:, None, :]
+    s = np.sin(angles)[:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty(x.shape, dtype=np.float64)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Workload descriptions
+# --------------------------------------------------------------------------------------
+
+def split_offsets(S: int, P: int) -> List[int]:
+    """Offsets of P contiguous partitions of S tokens; the first S mod P get one more token."""
+    base, rem = divmod(S, P)
+    offs = [0]
+    for p in range(P):
+        offs.append(offs[-1] + base + (1 if p < rem else 0))
+    return offs
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    H: int
+    D: int
+    grid: Tuple[int, ...]          # latent token grid; tokens are row-major over it
+    P: int                         # KV partitions
+    q_token_range: Tuple[int, int]  # query tokens [a, b) of the sequence
+    q_offsets: List[int]           # query-block offsets, relative to q_token_range[0]
+    local_part: List[int]          # each query block's own partition
+    group_offsets: List[int]       # groups of adjacent partitions
+    recompute_groups: int          # groups recomputed per query block (local one included)
+    mode: str                      # "distance" | "wdelta" | "anchor"
+    anchor_every: int = 0          # anchor period for "wdelta"
+    steps: int = 1                 # denoising steps in the trajectory
+    prev_scale: float = 0.0        # X_prev = X - prev_scale * N(0,1)  (single-step configs)
+    drift_scale: float = 0.0       # X_t = X_{t-1} + drift_scale * N(0,1)  (trajectories)
+    seed: int = 0
+    B: int = 1
+    description: str = ""
+
+    @property
+    def S_kv(self) -> int:
+        return int(np.prod(self.grid))
+
+    @property
+    def S_q(self) -> int:
+        return self.q_token_range[1] - self.q_token_range[0]
+
+    @property
+    def kv_offsets(self) -> List[int]:
+        return split_offsets(self.S_kv, self.P)
+
+    @property
+    def n_qb(self) -> int:
+        return len(self.q_offsets) - 1
+
+    @property
+    def G(self) -> int:
+        return len(self.group_offsets) - 1
+
+
+def _grid_workload(name, H, D, grid, P, group_size, K, mode, seed, **kw) -> Workload:
+    S = int(np.prod(grid))
+    offs = split_offsets(S, P)
+    return Workload(name=name, H=H, D=D, grid=tuple(grid), P=P, q_token_range=(0, S),
+                    q_offsets=list(offs), local_part=list(range(P)),
+                    group_offsets=list(range(0, P + 1, group_size)), recompute_groups=K,
+                    mode=mode, seed=seed, **kw)
+
+
+WORKLOAD_NAMES = ["tiny", "image_anchor", "video720p", "share32", "longvideo"]
+
+_FULL_GRIDS = {"tiny": (16, 16), "image_anchor": (64, 64), "video720p": (21, 45, 80),
+               "share32": (21, 45, 80), "longvideo": (41, 45, 80)}
+
+
+def workload(name: str, grid: Optional[Sequence[int]] = None, H: Optional[int] = None) -> Workload:
+    """The named workload; `grid` and `H` shrink it (same partition count, group layout,
+    selection rule and noise) for parity cases the oracle finishes in seconds.
+
+    Seeds are 1000 + the workload's index in WORKLOAD_NAMES."""
+    full = grid is None
+    g = tuple(_FULL_GRIDS[name] if grid is None else grid)
+    S = int(np.prod(g))
+    seed = 1000 + WORKLOAD_NAMES.index(name)
+    tag = "" if full else "@" + "x".join(map(str, g))
+    if name == "tiny":
+        w = Workload(name="tiny" + tag, H=2 if H is None else H, D=64, grid=g, P=4,
+                     q_token_range=(0, S), q_offsets=[0, S], local_part=[0],
+                     group_offsets=[0, 2, 4], recompute_groups=1, mode="distance",
+                     prev_scale=0.05, seed=seed,
+                     description="S=256 (16x16, 2D RoPE), H=2, D=64, P=4 x 64; {0,1} recomputed, "
+                                 "{2,3} reused from states of X_prev = X - 0.05 N(0,1)")
+    elif name == "image_anchor":
+        w = _grid_workload("image_anchor" + tag, 24 if H is None else H, 128, g, 8, 1, 8, "anchor", seed,
+                           description="S=4096 (64x64, 2D RoPE), H=24, D=128, P=8 row bands, "
+                                       "all partitions recomputed (anchor step)")
+    elif name == "video720p":
+        w = _grid_workload("video720p" + tag, 40 if H is None else H, 128, g, 16, 2, 4, "distance", seed,
+                           prev_scale=0.05,
+                           description="S=75,600 (21x45x80, 3D RoPE), H=40, D=128, P=16, groups of 2, "
+                                       "4 of 8 groups recomputed per query block by distance")
+    elif name == "share32":
+        offs = split_offsets(S, 32)
+        w = Workload(name="share32" + tag, H=40 if H is None else H, D=128, grid=g, P=32,
+                     q_token_range=(0, offs[1]), q_offsets=[0, offs[1]], local_part=[0],
+                     group_offsets=list(range(33)), recompute_groups=1 + math.ceil(0.25 * 31),
+                     mode="distance", prev_scale=0.05, seed=seed,
+                     description="one device's share of a 32-way split: local queries = partition 0, "
+                                 "KV = 75,600 tokens in 32 partitions; 9 recomputed, 23 reused")
+    elif name == "longvideo":
+        w = _grid_workload("longvideo" + tag, 40 if H is None else H, 128, g, 32, 4, 4, "wdelta", seed,
+                           anchor_every=5, steps=10, drift_scale=0.02,
+                           description="S=147,600 (41x45x80, 3D RoPE), H=40, D=128, P=32 in groups of 4, "
+                                       "anchor every 5 steps, w*delta group planner")
+    else:
+        raise KeyError(name)
+    return w
+
+
+# --------------------------------------------------------------------------------------
+# Seeded draws
+# --------------------------------------------------------------------------------------
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _draw_chunk(seed: int, tensor: int, chunk: int, n: int, H: int, D: int) -> np.ndarray:
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=(tensor, chunk))
+    rng = np.random.Generator(np.random.PCG64(ss))
+    return rng.standard_normal((n, H, D), dtype=np.float32)
+
+
+def normal_tokens(seed: int, tensor: int, start: int, stop: int, H: int, D: int) -> np.ndarray:
+    """Standard-normal float32 values [stop-start, H, D] of stream `tensor` for tokens [start, stop)."""
+    out = np.empty((stop - start, H, D), dtype=np.float32)
+    c0 = start // CHUNK_TOKENS
+    c1 = (stop + CHUNK_TOKENS - 1) // CHUNK_TOKENS
+
+    def job(c):
+        a = c * CHUNK_TOKENS
+        full = _draw_chunk(seed, tensor, c, CHUNK_TOKENS, H, D)
+        lo, hi = max(a, start), min(a + CHUNK_TOKENS, stop)
+        out[lo - start:hi - start] = full[lo - a:hi - a]
+
+    chunks = list(range(c0, c1))
+    if len(chunks) <= 2:
+        for c in chunks:
+            job(c)
+    else:
+        with _cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(job, chunks))
+    return out
+
+
+def _finish(w: Workload, x32: np.ndarray, start: int, stop: int, rope: bool) -> np.ndarray:
+    """RoPE (for Q, K) in float64, then float32, then bfloat16 bits.  Processed in token chunks."""
+    out = np.empty(x32.shape, dtype=np.uint16)
+    step = 4096
+
+    def job(a):
+        b = min(a + step, stop - start)
+        blk = x32[a:b]
+        if rope:
+            ang = rope_angles(w.grid, w.D, start + a, start + b)
+            blk = apply_rope(blk, ang).astype(np.float32)
+        out[a:b] = f32_to_bf16_bits(blk)
+
+    starts = list(range(0, stop - start, step))
+    if len(starts) <= 1:
+        for a in starts:
+            job(a)
+    else:
+        with _cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(job, starts))
+    return out
+
+
+@dataclasses.dataclass
+class StepInputs:
+    """bfloat16 bit patterns [B, S, H, D] of one denoising step's Q (query tokens only), K, V."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+
+
+def base_f32(w: Workload, which: int, start: int, stop: int) -> np.ndarray:
+    return normal_tokens(w.seed, which, start, stop, w.H, w.D)
+
+
+def step_f32(w: Workload, which: int, step: int, start: int, stop: int) -> np.ndarray:
+    """Pre-RoPE float32 values of tensor `which` at trajectory step `step` (0 = base draw).
+
+    Trajectory: X_t = X_{t-1} + drift_scale * N_t, accumulated in float32.
+    Single-step configs use step = -1 for the previous step's inputs:
+    X_prev = X - prev_scale * N."""
+    x = base_f32(w, which, start, stop)
+    if step == -1:
+        n = normal_tokens(w.seed, noise_id(1, which), start, stop, w.H, w.D)
+        return x - np.float32(w.prev_scale) * n
+    for t in range(1, step + 1):
+        n = normal_tokens(w.seed, noise_id(t, which), start, stop, w.H, w.D)
+        x = x + np.float32(w.drift_scale) * n
+    return x
+
+
+def make_tensor(w: Workload, which: int, step: int = 0, token_range: Optional[Tuple[int, int]] = None) -> np.ndarray:
+    """bf16 bits [B, n, H, D] of Q/K/V at `step` for tokens `token_range` (default: all of its tokens)."""
+    if token_range is None:
+        token_range = w.q_token_range if which == T_Q else (0, w.S_kv)
+    a, b = token_range
+    x = step_f32(w, which, step, a, b)
+    bits = _finish(w, x, a, b, rope=(which != T_V))
+    return bits[None]
+
+
+def make_step(w: Workload, step: int = 0) -> StepInputs:
+    return StepInputs(q=make_tensor(w, T_Q, step), k=make_tensor(w, T_K, step), v=make_tensor(w, T_V, step))
+
+
+def q_rows(w: Workload, step: int, rows: np.ndarray) -> np.ndarray:
+    """bf16 bits [1, len(rows), H, D] of the query rows `rows` (indices relative to q_token_range)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((1, len(rows), w.H, w.D), dtype=np.uint16)
+    a0 = w.q_token_range[0]
+    # contiguous runs keep regeneration cheap
+    i = 0
+    while i < len(rows):
+        j = i
+        while j + 1 < len(rows) and rows[j + 1] == rows[j] + 1:
+            j += 1
+        out[0, i:j + 1] = make_tensor(w, T_Q, step, (a0 + rows[i], a0 + rows[j] + 1))[0]
+        i = j + 1
+    return out
+
+
+def to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bits to float64."""
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def sample_rows(w: Workload, tiles_per_block: int = 2, tile: int = 128) -> np.ndarray:
+    """Deterministic query-row sample: the first and last `tile` rows of every query block
+    (tiles_per_block=2), so both a full leading tile and the ragged tail are covered."""
+    rows = []
+    for i in range(w.n_qb):
+        a, b = w.q_offsets[i], w.q_offsets[i + 1]
+        if b - a <= tiles_per_block * tile:
+            rows.append(np.arange(a, b))
+            continue
+        rows.append(np.arange(a, a + tile))
+        if tiles_per_block >= 2:
+            rows.append(np.arange(b - tile, b))
+    return np.unique(np.concatenate(rows))
