@@ -1,0 +1,221 @@
+"""Benchmark of the selective attention step on one MI355X.
+
+Workload (default): the 720p video layer, S = 75,600 tokens (21x45x80 latent grid, 3D
+RoPE), H = 40, D = 128, bf16, P = 16 KV partitions, 16 query blocks, groups of two
+adjacent partitions, 4 of 8 groups recomputed per query block by distance.  The state
+cache is filled beforehand by an all-recompute step on the previous step's inputs
+(X_prev = X - 0.05 N(0,1)).
+
+One step = the whole hot path on one batch: host planner decision and work list, partition
+attention with the cache update and the local-change partial sums, state merge, and the
+local-change reduction.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  `value` = recomputed-attention FLOP per step / step wall time.
+`roofline` = the partition-attention kernel against bf16 dense MFMA peak; `roofline_merge`
+= the merge kernel against HBM peak; both from HIP events on the launch stream.
+`cpu_baseline` = the fp64 oracle timed on a bounded row sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_flop(w: W.Workload, mask: np.ndarray) -> float:
+    """4 D H sum over recomputed (block i, partition p) of |i| |p|  (QK^T and PV)."""
+    qs = np.diff(w.q_offsets)
+    ks = np.diff(w.kv_offsets)
+    return float(4 * w.D * w.H * np.sum(mask * np.outer(qs, ks)))
+
+
+def merge_bytes(w: W.Workload) -> float:
+    """S_q H [P (2D + 4) + (2D + 4)]: read every state (bf16 O, f32 lse) once, write O and lse."""
+    return float(w.S_q * w.H * (w.P * (2 * w.D + 4) + (2 * w.D + 4)))
+
+
+def cpu_baseline(w: W.Workload, X: "W.StepInputs", mask: np.ndarray, rows_per_block: int) -> dict:
+    """Time the oracle's step work (recomputed partition states + merge) on a row sample."""
+    import oracle
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    rows = np.concatenate([np.arange(w.q_offsets[i], w.q_offsets[i] + min(rows_per_block, w.q_offsets[i + 1] - w.q_offsets[i]))
+                           for i in range(w.n_qb)])
+    q = W.to_f64(X.q[0][rows])
+    k = W.to_f64(X.k[0])
+    v = W.to_f64(X.v[0])
+    cache = oracle.StateCache.empty(rows, w.P, w.H, w.D, w.n_qb)
+    # reused slots hold placeholder states: this leg measures time, parity is tested elsewhere
+    sizes = np.diff(w.kv_offsets)
+    for p in range(w.P):
+        cache.exact_lse[p][:] = math.log(max(sizes[p], 1))
+        cache.stored_lse[p][:] = math.log(max(sizes[p], 1))
+    cache.valid[:] = True
+    t0 = time.perf_counter()
+    oracle.selective_step(q, k, v, rows, w.q_offsets, w.kv_offsets, mask, cache, 1.0 / math.sqrt(w.D))
+    dt = time.perf_counter() - t0
+    blk = oracle.block_of_rows(rows, w.q_offsets)
+    flop = float(4 * w.D * w.H * sum(int(mask[b].astype(np.int64) @ sizes) for b in blk))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{len(rows)} of {w.S_q} query rows (first {rows_per_block} of each of the {w.n_qb} "
+                      f"query blocks), all {w.H} heads: fp64 states of the recomputed partitions and the "
+                      f"{w.P}-state merge; reused slots hold placeholder states"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="video720p", choices=["video720p", "share32", "image_anchor", "longvideo"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="oracle sample rows per query block")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards by query block across GPUs, which is not built here)"}))
+        return 2
+
+    import torch
+    from partitioned_state_reuse_amd import api
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    dev = torch.device("cuda:0")
+    w = W.workload(args.workload)
+    log(f"[bench] workload {w.name}: S_q={w.S_q} S_kv={w.S_kv} H={w.H} D={w.D} P={w.P} n_qb={w.n_qb}")
+    t0 = time.time()
+    X = W.make_step(w, 0)
+    Xp = W.make_step(w, -1) if w.prev_scale else X
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    def dev_t(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = dev_t(X.q), dev_t(X.k), dev_t(X.v)
+    sa = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part)
+    mode = "anchor" if w.mode == "anchor" else "distance"
+    planner = api.Planner(w.n_qb, w.P, w.group_offsets, w.local_part, w.anchor_every or 0,
+                          w.recompute_groups, mode)
+    # fill the cache with the previous step's states (not timed)
+    qp, kp, vp = dev_t(Xp.q), dev_t(Xp.k), dev_t(Xp.v)
+    sa.step(qp, kp, vp, np.ones((w.n_qb, w.P), np.uint8))
+    torch.cuda.synchronize()
+    del qp, kp, vp
+    stream = torch.cuda.current_stream()
+    want_delta = True
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+
+    def one_step(t, events=None):
+        mask, _ = planner.next(t)
+        if events:
+            events[0].record(stream)
+        api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
+                                local_part=w.local_part, delta_partials=sa.workspace if want_delta else None,
+                                stream=stream)
+        if events:
+            events[1].record(stream)
+        api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
+        if events:
+            events[2].record(stream)
+        if want_delta:
+            api.local_change_finalize(sa.workspace, 1, w.S_q, w.H, w.D, w.q_offsets, sa.delta, stream=stream)
+        if events:
+            events[3].record(stream)
+        return mask
+
+    for t in range(args.warmup):
+        mask = one_step(t + 1)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for t in range(args.steps):
+        mask = one_step(t + 1, ev[t])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall / max(args.steps, 1) * 1e3
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    fin_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    flop = attn_flop(w, mask)
+    mbytes = merge_bytes(w)
+    attn_tflops = flop / (attn_ms * 1e-3) / 1e12
+    merge_gbs = mbytes / (merge_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_step:.3f} ms  attention {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s)  "
+        f"merge {merge_ms:.3f} ms ({merge_gbs:.0f} GB/s)  finalize {fin_ms:.4f} ms")
+
+    # plain device copy of 4 GiB as the achievable-bandwidth reference (and PMC calibration)
+    src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(3):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s")
+
+    result = {
+        "metric": "recomputed-attn TFLOP/s + merge GB/s at 75.6k tokens, % of MFMA/HBM peak",
+        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V with 3D RoPE, bf16",
+        "config": {"workload": w.name, "tokens": w.S_kv, "query_tokens": w.S_q, "heads": w.H, "head_dim": w.D,
+                   "partitions": w.P, "query_blocks": w.n_qb, "group_size": int(np.diff(w.group_offsets)[0]),
+                   "recomputed_groups_per_block": w.recompute_groups,
+                   "recomputed_pairs": int(mask.sum()), "reused_pairs": int(mask.size - mask.sum()),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "partition_attention_kernel<128>", "ms": round(attn_ms, 4),
+                     "algorithmic_flop": flop},
+        "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                           "kernel": "state_merge_kernel<128,16>", "ms": round(merge_ms, 4),
+                           "algorithmic_bytes": mbytes, "device_copy_gbs": round(copy_gbs, 1)},
+        "local_change_finalize_ms": round(fin_ms, 5),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a row sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, X, mask, args.cpu_rows)
+        log(f"[bench] oracle {result['cpu_baseline']['seconds']} s")
+    planner.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,221 @@
+/*
+ * dit_attn.h -- C ABI of the partitioned DiT self-attention library for MI355X (gfx950).
+ *
+ * The operation (DiTango: Cost-Effective Parallel Diffusion Generation with Selective
+ * Attention State Reuse, technical summary, "Methodology"): non-causal self-attention of
+ * query tokens over a key/value sequence that is split into P contiguous KV partitions.
+ *
+ *   - Attention over one partition p gives the attention state (O_p, lse_p) of every query
+ *     row and head: s_j = scale * q . k_j over the keys j of p, lse_p = ln sum_j e^{s_j},
+ *     O_p = sum_j e^{s_j - lse_p} v_j   ("Methodology §2, State Composition").
+ *   - States compose associatively and commutatively by LSE-weighted combination:
+ *     lse = ln sum_p e^{lse_p}, O = sum_p e^{lse_p - lse} O_p.  The library caches the
+ *     per-partition states, not raw K/V.
+ *   - A recompute mask chooses, per query block i and partition p, whether the state of
+ *     (i, p) is computed from scratch or taken from the cache filled at an earlier
+ *     denoising step ("Methodology §1, Anchor-Guided Selection Planner").
+ *   - Anchor steps recompute every partition and refresh the partition importance
+ *     w_ip = mean over block i's rows and heads of e^{lse_p - lse}; between anchors the
+ *     change of each block's always-recomputed local state,
+ *     delta_i = ||O_loc(t) - O_loc(t-1)||_F / ||O_loc(t-1)||_F, stands in for how the other
+ *     states evolve ("Methodology §1, Error Modeling, Anchor Steps, Online Prediction").
+ *   - A host-side planner turns w and delta into the next step's mask, per group of
+ *     adjacent partitions ("Methodology §1, Group-wise Strategy").
+ *
+ * Conventions shared by every call:
+ *   - Device pointers are caller-owned device memory (e.g. allocated by PyTorch); the
+ *     library allocates and frees no device or pinned memory and keeps no pointer after a
+ *     call returns.  Host pointers are only read during the call.
+ *   - Layouts (row-major, bf16 = bfloat16, 2 bytes):
+ *       q            [B, S_q, H, D]  bf16      (RoPE already applied)
+ *       k, v         [B, S_kv, H, D] bf16
+ *       cache_o      [P, B, S_q, H, D] bf16    state cache: output of each partition
+ *       cache_lse    [P, B, H, S_q] f32        state cache: natural-log lse of each partition
+ *       out          [B, S_q, H, D] bf16       merged output
+ *       lse          [B, H, S_q] f32           merged lse
+ *     All device buffers must be 16-byte aligned.
+ *   - q_offsets [n_qb+1]: query-block offsets, q_offsets[0] = 0, strictly increasing,
+ *     q_offsets[n_qb] = S_q.  kv_offsets [P+1]: partition offsets, kv_offsets[0] = 0,
+ *     non-decreasing (empty partitions allowed), kv_offsets[P] = S_kv.
+ *     1 <= n_qb <= DIT_MAX_BLOCKS, 1 <= P <= DIT_MAX_PARTITIONS.
+ *   - recompute [n_qb * P] (row-major, block-major): 1 = compute the state of (i, p) and
+ *     write it into the cache slot, 0 = reuse the cached slot.  Any other value is an error.
+ *   - D must be 64 or 128.
+ *   - Every call validates all arguments on the host before it enqueues anything: on any
+ *     error return no buffer is touched and nothing is enqueued.  Calls are asynchronous on
+ *     `stream` (a hipStream_t; NULL = the null stream) and never synchronise.  A failed
+ *     launch returns DIT_ERR_HIP; faults inside a kernel surface at the caller's next
+ *     synchronisation.  There is no global mutable state: calls are reentrant.  No C++
+ *     exception crosses the ABI (DIT_ERR_INTERNAL).
+ *   - Results are deterministic: every reduction has a fixed order and no floating-point
+ *     atomics are used, so repeated calls give bitwise-equal outputs.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_MAX_BLOCKS 64
+#define DIT_MAX_PARTITIONS 64
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_ERR_NULL = -1,          /* a required pointer is NULL */
+  DIT_ERR_SHAPE = -2,         /* B, S_q, S_kv, H, n_qb or P out of range */
+  DIT_ERR_OFFSETS = -3,       /* q_offsets / kv_offsets / group offsets malformed */
+  DIT_ERR_MASK = -4,          /* recompute value not 0/1, local partition not recomputed, bad local_part */
+  DIT_ERR_CACHE_INVALID = -5, /* reuse (or delta) of a cache slot that cache_valid marks never computed */
+  DIT_ERR_WORKSPACE = -6,     /* workspace NULL or smaller than dit_attn_workspace_bytes() */
+  DIT_ERR_UNSUPPORTED = -7,   /* D not in {64, 128}, or a mode this build does not implement */
+  DIT_ERR_HIP = -8,           /* a HIP launch failed */
+  DIT_ERR_INTERNAL = -9       /* unexpected internal error */
+} dit_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *dit_status_string(int status);
+
+/* Bytes of device workspace dit_attn_partitioned needs for these sizes (for the
+ * local-change partial sums).  Returns 0 if the sizes are invalid. */
+size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P);
+
+/*
+ * One selective attention step (partition attention, cache update, merge, and optionally
+ * importance and local change).  Equivalent to dit_partition_attention, then
+ * dit_state_merge, then dit_importance / dit_local_change_finalize when requested.
+ *
+ *   softmax_scale      > 0, or <= 0 for 1/sqrt(D)
+ *   local_part         host [n_qb] or NULL: each block's own partition.  When given, the
+ *                      local partition of every block must be recomputed (DIT_ERR_MASK).
+ *   cache_valid        host [n_qb * P] or NULL: 1 = slot holds a state from an earlier step.
+ *                      When given, reusing a slot marked 0 is DIT_ERR_CACHE_INVALID.
+ *   importance_out     device [B, n_qb, P] f32 or NULL: w_ip of this step's states.
+ *   delta_out          device [B, n_qb] f32 or NULL: delta_i of the local states against the
+ *                      states the local slots held before this call.  Needs local_part and
+ *                      a workspace; with cache_valid given the local slots must be valid.
+ *   workspace          device, >= dit_attn_workspace_bytes(...) when delta_out is given,
+ *                      else may be NULL.  Contents on entry are ignored.
+ */
+int dit_attn_partitioned(const void *q, const void *k, const void *v,
+                         int B, int S_q, int S_kv, int H, int D,
+                         const int32_t *q_offsets, int n_qb,
+                         const int32_t *kv_offsets, int P,
+                         const int32_t *local_part,
+                         const uint8_t *recompute,
+                         const uint8_t *cache_valid,
+                         void *cache_o, float *cache_lse,
+                         void *out, float *lse,
+                         float softmax_scale,
+                         float *importance_out,
+                         float *delta_out,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * Partition attention and cache update only: for every (i, p) with recompute = 1, compute
+ * the state of block i's query rows over partition p's keys and write it into cache slot
+ * (p, rows of i); other slots are untouched.  bf16 MFMA products, fp32 accumulation and
+ * softmax.  An empty partition writes O = 0, lse = -inf.
+ *   delta_partials     device or NULL.  When given (with local_part), the kernel also writes,
+ *                      per (query tile, head) of each block's local partition, the sums
+ *                      sum (O_new - O_old)^2 and sum O_old^2 over the tile's rows and D,
+ *                      where O_old is the slot's content before this call and O_new the bf16
+ *                      value written.  Layout and size are internal: pass the workspace of
+ *                      dit_attn_workspace_bytes and finish with dit_local_change_finalize.
+ */
+int dit_partition_attention(const void *q, const void *k, const void *v,
+                            int B, int S_q, int S_kv, int H, int D,
+                            const int32_t *q_offsets, int n_qb,
+                            const int32_t *kv_offsets, int P,
+                            const int32_t *local_part,
+                            const uint8_t *recompute,
+                            void *cache_o, float *cache_lse,
+                            float softmax_scale,
+                            void *delta_partials, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * State merge: for every query row and head, compose the P cached states (all P slots,
+ * as the partition-attention call left them) into out / lse by LSE-weighted combination in
+ * fp32; states with lse = -inf carry no weight; if every state is empty, out = 0 and
+ * lse = -inf.  n_qb/q_offsets are accepted for validation symmetry and may be 1 / NULL.
+ */
+int dit_state_merge(const void *cache_o, const float *cache_lse,
+                    int B, int S_q, int H, int D, int P,
+                    void *out, float *lse,
+                    void *stream);
+
+/*
+ * Partition importance from the cached states and the merged lse of this step:
+ * importance_out[b, i, p] = mean over rows r of block i and heads h of
+ * e^{cache_lse[p, b, h, r] - lse[b, h, r]}  (0 for empty partitions).
+ */
+int dit_importance(const float *cache_lse, const float *lse,
+                   int B, int S_q, int H, int P,
+                   const int32_t *q_offsets, int n_qb,
+                   float *importance_out,
+                   void *stream);
+
+/*
+ * Finish the local-change reduction started by dit_partition_attention:
+ * delta_out[b, i] = sqrt(sum (O_new - O_old)^2) / sqrt(sum O_old^2) over block i's rows,
+ * heads and D (NaN if the old state is all zero).
+ */
+int dit_local_change_finalize(const void *delta_partials, size_t workspace_bytes,
+                              int B, int S_q, int H, int D,
+                              const int32_t *q_offsets, int n_qb,
+                              float *delta_out,
+                              void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Host-side group planner ("Methodology §1, Anchor-Guided Selection Planner").
+ *
+ * Groups are runs of adjacent partitions given by group_offsets [G+1] (0 = first, strictly
+ * increasing, last = P).  Each block's local group (the group holding local_part[i]) is
+ * always recomputed.  Modes:
+ *   DIT_PLAN_WDELTA   anchor step when step % anchor_every == 0 (all partitions); otherwise
+ *                     the K-1 other groups with the largest predicted reuse error
+ *                     e_ig = w_ig * sum_{tau = last_ig+1..step} dhat_i(tau)
+ *                     (w_ig = sum of the member partitions' importance at the last anchor;
+ *                     last_ig = step of the group's last recompute; dhat_i(tau) = delta_i(tau)
+ *                     where observed, else the latest delta observed before tau, else 1.0),
+ *                     ties broken by smaller group distance min_{p in g} |p - local_part[i]|,
+ *                     then by lower group index.  e is evaluated in double precision.
+ *   DIT_PLAN_DISTANCE the K-1 other groups ordered by (distance, index); never an anchor.
+ *   DIT_PLAN_ANCHOR   every step is an anchor step.
+ * K = recompute_groups (1 <= K <= G).
+ * ------------------------------------------------------------------------------------ */
+typedef struct dit_planner dit_planner;
+
+enum { DIT_PLAN_WDELTA = 0, DIT_PLAN_DISTANCE = 1, DIT_PLAN_ANCHOR = 2 };
+
+/* Create a planner; *out receives the handle (free with dit_planner_destroy). */
+int dit_planner_create(int n_qb, int P, const int32_t *group_offsets, int G,
+                       const int32_t *local_part, int anchor_every, int recompute_groups,
+                       int mode, dit_planner **out);
+
+/* Decide step `step`: mask_out host [n_qb * P] (1 = recompute); groups_out host
+ * [n_qb * G] or NULL receives the chosen groups per block (local group first, then in rank
+ * order; unused entries -1).  Records the chosen groups as refreshed at `step`. */
+int dit_planner_next(dit_planner *pl, int step, uint8_t *mask_out, int32_t *groups_out);
+
+/* Report step `step`'s measurements: importance host [n_qb * P] f32 or NULL (replaces
+ * the group importance; normally given at anchor steps), delta host [n_qb] f32 or NULL
+ * (non-finite entries are ignored). */
+int dit_planner_observe(dit_planner *pl, int step, const float *importance, const float *delta);
+
+/* Predicted reuse error e_ig (host [n_qb * G] doubles) that dit_planner_next(step) would
+ * rank by, for inspection and testing. */
+int dit_planner_scores(const dit_planner *pl, int step, double *scores_out);
+
+void dit_planner_destroy(dit_planner *pl);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

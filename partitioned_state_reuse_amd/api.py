@@ -1,0 +1,197 @@
+"""Python binding of the C ABI (include/dit_attn.h): argument marshalling only.
+
+PyTorch supplies device memory and the stream; every step of the path runs in the HIP
+library.  Errors from the library raise DitError(code, message).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+
+DIT_PLAN_WDELTA, DIT_PLAN_DISTANCE, DIT_PLAN_ANCHOR = 0, 1, 2
+MODES = {"wdelta": DIT_PLAN_WDELTA, "distance": DIT_PLAN_DISTANCE, "anchor": DIT_PLAN_ANCHOR}
+
+
+class DitError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{message} (status {code})")
+        self.code = code
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise DitError(code, _lib.lib().dit_status_string(code).decode())
+
+
+def status_string(code: int) -> str:
+    return _lib.lib().dit_status_string(code).decode()
+
+
+def _i32(seq) -> ctypes.Array:
+    a = np.ascontiguousarray(np.asarray(seq, dtype=np.int32))
+    return (ctypes.c_int32 * len(a))(*a.tolist())
+
+
+def _u8(arr) -> ctypes.Array:
+    a = np.ascontiguousarray(np.asarray(arr, dtype=np.uint8)).reshape(-1)
+    return (ctypes.c_uint8 * len(a)).from_buffer_copy(a.tobytes())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor) -> Tuple[int, int, int, int, int]:
+    B, S_q, H, D = q.shape
+    Bk, S_kv, Hk, Dk = k.shape
+    if (B, H, D) != (Bk, Hk, Dk):
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    return B, S_q, S_kv, H, D
+
+
+def _require(t: torch.Tensor, dtype, shape, name: str) -> None:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: need contiguous {dtype} cuda tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+
+
+def workspace_bytes(B: int, S_q: int, H: int, D: int, n_qb: int, P: int) -> int:
+    return int(_lib.lib().dit_attn_workspace_bytes(B, S_q, H, D, n_qb, P))
+
+
+def attn_partitioned(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, out, lse, *,
+                     local_part=None, cache_valid=None, scale: float = 0.0, importance_out=None,
+                     delta_out=None, workspace=None, stream=None) -> None:
+    """One selective step: dit_attn_partitioned.  Tensors are device tensors in the
+    layouts of include/dit_attn.h; offsets, mask, local_part and cache_valid are host
+    sequences/arrays."""
+    B, S_q, S_kv, H, D = _dims(q, k)
+    n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lib().dit_attn_partitioned(
+        _ptr(q), _ptr(k), _ptr(v), B, S_q, S_kv, H, D,
+        _i32(q_offsets), n_qb, _i32(kv_offsets), P,
+        None if local_part is None else _i32(local_part), _u8(recompute),
+        None if cache_valid is None else _u8(cache_valid),
+        _ptr(cache_o), _ptr(cache_lse), _ptr(out), _ptr(lse), float(scale),
+        _ptr(importance_out), _ptr(delta_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def partition_attention(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, *,
+                        local_part=None, scale: float = 0.0, delta_partials=None, stream=None) -> None:
+    B, S_q, S_kv, H, D = _dims(q, k)
+    n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
+    ws_bytes = 0 if delta_partials is None else delta_partials.numel() * delta_partials.element_size()
+    _check(_lib.lib().dit_partition_attention(
+        _ptr(q), _ptr(k), _ptr(v), B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
+        None if local_part is None else _i32(local_part), _u8(recompute), _ptr(cache_o), _ptr(cache_lse),
+        float(scale), _ptr(delta_partials), ws_bytes, _stream(stream)))
+
+
+def state_merge(cache_o, cache_lse, out, lse, *, stream=None) -> None:
+    P, B, S_q, H, D = cache_o.shape
+    _check(_lib.lib().dit_state_merge(_ptr(cache_o), _ptr(cache_lse), B, S_q, H, D, P, _ptr(out), _ptr(lse),
+                                      _stream(stream)))
+
+
+def importance(cache_lse, lse, q_offsets, importance_out, *, stream=None) -> None:
+    P, B, H, S_q = cache_lse.shape
+    _check(_lib.lib().dit_importance(_ptr(cache_lse), _ptr(lse), B, S_q, H, P, _i32(q_offsets),
+                                     len(q_offsets) - 1, _ptr(importance_out), _stream(stream)))
+
+
+def local_change_finalize(delta_partials, B, S_q, H, D, q_offsets, delta_out, *, stream=None) -> None:
+    ws_bytes = delta_partials.numel() * delta_partials.element_size()
+    _check(_lib.lib().dit_local_change_finalize(_ptr(delta_partials), ws_bytes, B, S_q, H, D, _i32(q_offsets),
+                                                len(q_offsets) - 1, _ptr(delta_out), _stream(stream)))
+
+
+class Planner:
+    """Host group planner (dit_planner_*)."""
+
+    def __init__(self, n_qb: int, P: int, group_offsets: Sequence[int], local_part: Sequence[int],
+                 anchor_every: int, recompute_groups: int, mode: str):
+        self.n_qb, self.P, self.G = n_qb, P, len(group_offsets) - 1
+        h = ctypes.c_void_p()
+        _check(_lib.lib().dit_planner_create(n_qb, P, _i32(group_offsets), self.G, _i32(local_part),
+                                             int(anchor_every), int(recompute_groups), MODES[mode],
+                                             ctypes.byref(h)))
+        self._h = h
+
+    def next(self, step: int) -> Tuple[np.ndarray, List[List[int]]]:
+        mask = (ctypes.c_uint8 * (self.n_qb * self.P))()
+        groups = (ctypes.c_int32 * (self.n_qb * self.G))()
+        _check(_lib.lib().dit_planner_next(self._h, int(step), mask, groups))
+        m = np.frombuffer(mask, dtype=np.uint8).reshape(self.n_qb, self.P).copy()
+        g = np.frombuffer(groups, dtype=np.int32).reshape(self.n_qb, self.G)
+        return m, [[int(x) for x in row if x >= 0] for row in g]
+
+    def observe(self, step: int, importance=None, delta=None) -> None:
+        def f32(a):
+            if a is None:
+                return None
+            arr = np.ascontiguousarray(np.asarray(a, dtype=np.float32)).reshape(-1)
+            return (ctypes.c_float * len(arr)).from_buffer_copy(arr.tobytes())
+        _check(_lib.lib().dit_planner_observe(self._h, int(step), f32(importance), f32(delta)))
+
+    def scores(self, step: int) -> np.ndarray:
+        out = (ctypes.c_double * (self.n_qb * self.G))()
+        _check(_lib.lib().dit_planner_scores(self._h, int(step), out))
+        return np.frombuffer(out, dtype=np.float64).reshape(self.n_qb, self.G).copy()
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _lib.lib().dit_planner_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class SelectiveAttention:
+    """Owns one layer's state cache on the GPU and runs selective steps.
+
+    Keeps the per-slot validity bitmap that the C ABI checks (a slot becomes valid once
+    its state has been computed) and the local-change workspace."""
+
+    def __init__(self, B: int, S_q: int, S_kv: int, H: int, D: int, q_offsets: Sequence[int],
+                 kv_offsets: Sequence[int], local_part: Sequence[int], device="cuda"):
+        self.B, self.S_q, self.S_kv, self.H, self.D = B, S_q, S_kv, H, D
+        self.q_offsets, self.kv_offsets = list(q_offsets), list(kv_offsets)
+        self.local_part = list(local_part)
+        self.n_qb, self.P = len(q_offsets) - 1, len(kv_offsets) - 1
+        self.cache_o = torch.empty((self.P, B, S_q, H, D), dtype=torch.bfloat16, device=device)
+        self.cache_lse = torch.empty((self.P, B, H, S_q), dtype=torch.float32, device=device)
+        self.out = torch.empty((B, S_q, H, D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((B, H, S_q), dtype=torch.float32, device=device)
+        self.importance = torch.empty((B, self.n_qb, self.P), dtype=torch.float32, device=device)
+        self.delta = torch.empty((B, self.n_qb), dtype=torch.float32, device=device)
+        nb = workspace_bytes(B, S_q, H, D, self.n_qb, self.P)
+        self.workspace = torch.empty(max(nb, 4) // 4, dtype=torch.float32, device=device)
+        self.valid = np.zeros((self.n_qb, self.P), dtype=np.uint8)
+
+    def step(self, q, k, v, recompute, *, want_importance=False, want_delta=False, scale=0.0, stream=None):
+        recompute = np.asarray(recompute, dtype=np.uint8).reshape(self.n_qb, self.P)
+        local_valid = all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
+        do_delta = want_delta and local_valid
+        attn_partitioned(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
+                         self.out, self.lse, local_part=self.local_part, cache_valid=self.valid, scale=scale,
+                         importance_out=self.importance if want_importance else None,
+                         delta_out=self.delta if do_delta else None,
+                         workspace=self.workspace if do_delta else None, stream=stream)
+        self.valid |= recompute
+        return do_delta

@@ -1,0 +1,260 @@
+// C ABI of the partitioned-attention library: argument validation, work descriptions and
+// kernel launches.  See include/dit_attn.h for the contract of every entry point.
+#include <math.h>
+#include <string.h>
+
+#include <exception>
+
+#include "launch.h"
+
+namespace {
+
+using dit::AttnDesc;
+using dit::BlockDesc;
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_dims(int B, int S_q, int S_kv, int H, int D) {
+  if (B < 1 || S_q < 0 || S_kv < 0 || H < 1) return DIT_ERR_SHAPE;
+  if (D != 64 && D != 128) return DIT_ERR_UNSUPPORTED;
+  // element offsets are 64-bit in the kernels; grid sizes and row indices are 32-bit
+  if ((int64_t)S_q * H > (int64_t)1 << 31 || (int64_t)S_kv * H > (int64_t)1 << 31)
+    return DIT_ERR_SHAPE;
+  return DIT_OK;
+}
+
+int check_q_offsets(const int32_t *q_offsets, int n_qb, int S_q) {
+  if (!q_offsets) return DIT_ERR_NULL;
+  if (n_qb < 1 || n_qb > DIT_MAX_BLOCKS) return DIT_ERR_SHAPE;
+  if (q_offsets[0] != 0 || q_offsets[n_qb] != S_q) return DIT_ERR_OFFSETS;
+  for (int i = 0; i < n_qb; ++i)
+    if (q_offsets[i + 1] <= q_offsets[i]) return DIT_ERR_OFFSETS;
+  return DIT_OK;
+}
+
+int check_kv_offsets(const int32_t *kv_offsets, int P, int S_kv) {
+  if (!kv_offsets) return DIT_ERR_NULL;
+  if (P < 1 || P > DIT_MAX_PARTITIONS) return DIT_ERR_SHAPE;
+  if (kv_offsets[0] != 0 || kv_offsets[P] != S_kv) return DIT_ERR_OFFSETS;
+  for (int p = 0; p < P; ++p)
+    if (kv_offsets[p + 1] < kv_offsets[p]) return DIT_ERR_OFFSETS;
+  return DIT_OK;
+}
+
+int num_tiles(int rows) { return (rows + dit::kBlockM - 1) / dit::kBlockM; }
+
+void fill_blocks(BlockDesc &bd, const int32_t *q_offsets, int n_qb) {
+  memset(&bd, 0, sizeof(bd));
+  bd.n_qb = n_qb;
+  bd.tile_prefix[0] = 0;
+  for (int i = 0; i <= n_qb; ++i) bd.q_off[i] = q_offsets[i];
+  for (int i = 0; i < n_qb; ++i)
+    bd.tile_prefix[i + 1] = bd.tile_prefix[i] + num_tiles(q_offsets[i + 1] - q_offsets[i]);
+  bd.n_tiles = bd.tile_prefix[n_qb];
+}
+
+size_t delta_ws_bytes(int B, int S_q, int H, int n_qb) {
+  // upper bound on the tile count of any split into n_qb blocks
+  const int64_t tiles = (int64_t)(S_q + dit::kBlockM - 1) / dit::kBlockM + n_qb;
+  return (size_t)B * (size_t)tiles * (size_t)H * 2 * sizeof(float);
+}
+
+// Validate and build the work description of one partition-attention launch.
+int build_attn(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H, int D,
+               const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P,
+               const int32_t *local_part, const uint8_t *recompute, const uint8_t *cache_valid,
+               const void *cache_o, const float *cache_lse, bool want_delta, const void *workspace,
+               size_t workspace_bytes, AttnDesc &desc) {
+  if (!q || !recompute || !cache_o || !cache_lse) return DIT_ERR_NULL;
+  if (S_kv > 0 && (!k || !v)) return DIT_ERR_NULL;  // no keys: k and v may be NULL
+  int st = check_dims(B, S_q, S_kv, H, D);
+  if (st) return st;
+  if ((st = check_q_offsets(q_offsets, n_qb, S_q))) return st;
+  if ((st = check_kv_offsets(kv_offsets, P, S_kv))) return st;
+  for (int e = 0; e < n_qb * P; ++e)
+    if (recompute[e] > 1) return DIT_ERR_MASK;
+  if (local_part) {
+    for (int i = 0; i < n_qb; ++i) {
+      if (local_part[i] < 0 || local_part[i] >= P) return DIT_ERR_MASK;
+      if (!recompute[i * P + local_part[i]]) return DIT_ERR_MASK;
+    }
+  }
+  if (cache_valid) {
+    for (int e = 0; e < n_qb * P; ++e)
+      if (!recompute[e] && !cache_valid[e]) return DIT_ERR_CACHE_INVALID;
+  }
+  if (want_delta) {
+    if (!local_part) return DIT_ERR_NULL;
+    if (!workspace) return DIT_ERR_WORKSPACE;
+    if (workspace_bytes < delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
+    if (cache_valid)
+      for (int i = 0; i < n_qb; ++i)
+        if (!cache_valid[i * P + local_part[i]]) return DIT_ERR_CACHE_INVALID;
+  }
+  memset(&desc, 0, sizeof(desc));
+  desc.B = B;
+  desc.H = H;
+  desc.S_q = S_q;
+  desc.S_kv = S_kv;
+  desc.n_qb = n_qb;
+  desc.P = P;
+  for (int i = 0; i <= n_qb; ++i) desc.q_off[i] = q_offsets[i];
+  for (int p = 0; p <= P; ++p) desc.kv_off[p] = kv_offsets[p];
+  for (int i = 0; i < n_qb; ++i)
+    desc.tile_prefix[i + 1] = desc.tile_prefix[i] + num_tiles(q_offsets[i + 1] - q_offsets[i]);
+  desc.n_tiles = desc.tile_prefix[n_qb];
+  for (int p = 0; p < P; ++p) {
+    uint64_t bm = 0;
+    int items = 0;
+    for (int i = 0; i < n_qb; ++i)
+      if (recompute[i * P + p]) {
+        bm |= (uint64_t)1 << i;
+        items += desc.tile_prefix[i + 1] - desc.tile_prefix[i];
+      }
+    desc.blocks_of_part[p] = bm;
+    desc.item_prefix[p + 1] = desc.item_prefix[p] + items;
+  }
+  desc.items_per_head = desc.item_prefix[P];
+  if ((int64_t)B * H * desc.items_per_head > INT32_MAX) return DIT_ERR_SHAPE;
+  for (int i = 0; i < n_qb; ++i) desc.local_part[i] = (want_delta && local_part) ? local_part[i] : -1;
+  return DIT_OK;
+}
+
+float scale_log2_of(float softmax_scale, int D) {
+  const float s = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  return s * 1.4426950408889634f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dit_status_string(int status) {
+  switch (status) {
+    case DIT_OK: return "DIT_OK";
+    case DIT_ERR_NULL: return "DIT_ERR_NULL: a required pointer is NULL";
+    case DIT_ERR_SHAPE: return "DIT_ERR_SHAPE: a size is out of range";
+    case DIT_ERR_OFFSETS: return "DIT_ERR_OFFSETS: offsets are malformed";
+    case DIT_ERR_MASK: return "DIT_ERR_MASK: recompute mask or local partition invalid";
+    case DIT_ERR_CACHE_INVALID: return "DIT_ERR_CACHE_INVALID: reuse of a never-computed cache slot";
+    case DIT_ERR_WORKSPACE: return "DIT_ERR_WORKSPACE: workspace missing or too small";
+    case DIT_ERR_UNSUPPORTED: return "DIT_ERR_UNSUPPORTED: unsupported head dim or mode";
+    case DIT_ERR_HIP: return "DIT_ERR_HIP: a HIP launch failed";
+    case DIT_ERR_INTERNAL: return "DIT_ERR_INTERNAL: internal error";
+    default: return "unknown status";
+  }
+}
+
+size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P) {
+  if (check_dims(B, S_q, 0, H, D) != DIT_OK) return 0;
+  if (n_qb < 1 || n_qb > DIT_MAX_BLOCKS || P < 1 || P > DIT_MAX_PARTITIONS) return 0;
+  return delta_ws_bytes(B, S_q, H, n_qb);
+}
+
+int dit_partition_attention(const void *q, const void *k, const void *v, int B, int S_q, int S_kv,
+                            int H, int D, const int32_t *q_offsets, int n_qb,
+                            const int32_t *kv_offsets, int P, const int32_t *local_part,
+                            const uint8_t *recompute, void *cache_o, float *cache_lse,
+                            float softmax_scale, void *delta_partials, size_t workspace_bytes,
+                            void *stream) {
+  try {
+    AttnDesc desc;
+    const bool want_delta = delta_partials != nullptr;
+    int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part,
+                        recompute, nullptr, cache_o, cache_lse, want_delta, delta_partials,
+                        workspace_bytes, desc);
+    if (st) return st;
+    if (dit::launch_partition_attention(D, q, k, v, cache_o, cache_lse, (float *)delta_partials, desc,
+                                        scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+int dit_state_merge(const void *cache_o, const float *cache_lse, int B, int S_q, int H, int D, int P,
+                    void *out, float *lse, void *stream) {
+  try {
+    if (!cache_o || !cache_lse || !out || !lse) return DIT_ERR_NULL;
+    int st = check_dims(B, S_q, 0, H, D);
+    if (st) return st;
+    if (P < 1 || P > DIT_MAX_PARTITIONS) return DIT_ERR_SHAPE;
+    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, as_stream(stream)) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+int dit_importance(const float *cache_lse, const float *lse, int B, int S_q, int H, int P,
+                   const int32_t *q_offsets, int n_qb, float *importance_out, void *stream) {
+  try {
+    if (!cache_lse || !lse || !importance_out) return DIT_ERR_NULL;
+    int st = check_dims(B, S_q, 0, H, 128);
+    if (st) return st;
+    if (P < 1 || P > DIT_MAX_PARTITIONS) return DIT_ERR_SHAPE;
+    if ((st = check_q_offsets(q_offsets, n_qb, S_q))) return st;
+    BlockDesc bd;
+    fill_blocks(bd, q_offsets, n_qb);
+    if (dit::launch_importance(cache_lse, lse, B, S_q, H, P, bd, importance_out, as_stream(stream)) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+int dit_local_change_finalize(const void *delta_partials, size_t workspace_bytes, int B, int S_q, int H,
+                              int D, const int32_t *q_offsets, int n_qb, float *delta_out, void *stream) {
+  try {
+    if (!delta_partials || !delta_out) return DIT_ERR_NULL;
+    int st = check_dims(B, S_q, 0, H, D);
+    if (st) return st;
+    if ((st = check_q_offsets(q_offsets, n_qb, S_q))) return st;
+    if (workspace_bytes < delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
+    BlockDesc bd;
+    fill_blocks(bd, q_offsets, n_qb);
+    if (dit::launch_delta_finalize((const float *)delta_partials, B, H, bd, delta_out, as_stream(stream)) !=
+        hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+int dit_attn_partitioned(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H,
+                         int D, const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P,
+                         const int32_t *local_part, const uint8_t *recompute, const uint8_t *cache_valid,
+                         void *cache_o, float *cache_lse, void *out, float *lse, float softmax_scale,
+                         float *importance_out, float *delta_out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  try {
+    if (!out || !lse) return DIT_ERR_NULL;
+    AttnDesc desc;
+    const bool want_delta = delta_out != nullptr;
+    int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
+                        cache_valid, cache_o, cache_lse, want_delta, workspace, workspace_bytes, desc);
+    if (st) return st;
+    hipStream_t s = as_stream(stream);
+    if (dit::launch_partition_attention(D, q, k, v, cache_o, cache_lse, want_delta ? (float *)workspace : nullptr,
+                                        desc, scale_log2_of(softmax_scale, D), s) != hipSuccess)
+      return DIT_ERR_HIP;
+    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, s) != hipSuccess)
+      return DIT_ERR_HIP;
+    BlockDesc bd;
+    fill_blocks(bd, q_offsets, n_qb);
+    if (importance_out &&
+        dit::launch_importance(cache_lse, lse, B, S_q, H, P, bd, importance_out, s) != hipSuccess)
+      return DIT_ERR_HIP;
+    if (want_delta && dit::launch_delta_finalize((const float *)workspace, B, H, bd, delta_out, s) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

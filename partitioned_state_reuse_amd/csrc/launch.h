@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (dit_attn.cpp) and the HIP kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dit_attn.h"
+
+namespace dit {
+
+constexpr int kBlockM = 128;  // query rows per attention workgroup (4 waves x 32 rows)
+constexpr int kBlockN = 64;   // keys per staged KV tile
+
+// Work description of one partition-attention launch, passed by value as a kernel
+// argument so that a launch needs no host-to-device copy.
+//
+// Items are (batch, head, partition p, query block i, query tile t) for every (i, p) whose
+// recompute flag is set.  Per (batch, head) the items are ordered by partition, then block,
+// then tile, so that consecutive workgroups read the same K/V partition.
+struct AttnDesc {
+  int32_t B, H, S_q, S_kv, n_qb, P;
+  int32_t items_per_head;                        // item_prefix[P]
+  int32_t n_tiles;                               // tile_prefix[n_qb]
+  int32_t q_off[DIT_MAX_BLOCKS + 1];
+  int32_t kv_off[DIT_MAX_PARTITIONS + 1];
+  int32_t tile_prefix[DIT_MAX_BLOCKS + 1];       // cumulative query tiles over blocks
+  int32_t item_prefix[DIT_MAX_PARTITIONS + 1];   // cumulative items over partitions
+  uint64_t blocks_of_part[DIT_MAX_PARTITIONS];   // bit i set: block i recomputes partition p
+  int32_t local_part[DIT_MAX_BLOCKS];            // -1: no local-change partials for block i
+};
+
+// Query-block offsets and tile prefix for the reductions.
+struct BlockDesc {
+  int32_t n_qb, n_tiles;
+  int32_t q_off[DIT_MAX_BLOCKS + 1];
+  int32_t tile_prefix[DIT_MAX_BLOCKS + 1];
+};
+
+hipError_t launch_partition_attention(int D, const void *q, const void *k, const void *v,
+                                      void *cache_o, float *cache_lse, float *delta_partials,
+                                      const AttnDesc &desc, float scale_log2, hipStream_t stream);
+
+hipError_t launch_state_merge(int D, int P, const void *cache_o, const float *cache_lse,
+                              void *out, float *lse, int B, int S_q, int H, hipStream_t stream);
+
+hipError_t launch_importance(const float *cache_lse, const float *lse, int B, int S_q, int H,
+                             int P, const BlockDesc &blocks, float *importance_out,
+                             hipStream_t stream);
+
+hipError_t launch_delta_finalize(const float *partials, int B, int H, const BlockDesc &blocks,
+                                 float *delta_out, hipStream_t stream);
+
+}  // namespace dit

@@ -1,0 +1,152 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header declares,
+validates arguments on the host (no kernel is launched: every call here fails validation
+before reaching the GPU), and its host planner matches the oracle planner bit-exactly."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_attn.h")
+
+from partitioned_state_reuse_amd import _lib  # noqa: E402
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_ ]*\**\s*\**(dit_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        import partitioned_state_reuse_amd.build as B
+        B.build()
+    return _lib.lib()
+
+
+def test_header_symbols_exported(L):
+    names = header_functions()
+    assert len(names) >= 12, names
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings(L):
+    for code in range(0, -10, -1):
+        s = L.dit_status_string(code).decode()
+        assert s.startswith("DIT_")
+    assert L.dit_status_string(5).decode() == "unknown status"
+
+
+def test_workspace_bytes(L):
+    assert L.dit_attn_workspace_bytes(1, 75600, 40, 128, 16, 16) == (591 + 16) * 40 * 8
+    assert L.dit_attn_workspace_bytes(1, 100, 4, 96, 1, 1) == 0      # unsupported D
+    assert L.dit_attn_workspace_bytes(1, 100, 4, 64, 0, 1) == 0      # no blocks
+    assert L.dit_attn_workspace_bytes(1, 100, 4, 64, 1, 65) == 0     # too many partitions
+
+
+def _call(L, *, q=1, k=1, v=1, B=1, S_q=8, S_kv=8, H=1, D=64, qo=(0, 8), ko=(0, 4, 8), local=(0,),
+          rec=(1, 0), valid=None, cache_o=1, cache_lse=1, out=1, lse=1, delta=None, ws=None, ws_bytes=0):
+    """dit_attn_partitioned with fake (never dereferenced) device pointers."""
+    i32 = lambda s: None if s is None else (ctypes.c_int32 * len(s))(*s)
+    u8 = lambda s: None if s is None else (ctypes.c_uint8 * len(s))(*s)
+    return L.dit_attn_partitioned(q, k, v, B, S_q, S_kv, H, D, i32(qo), len(qo) - 1 if qo else 1, i32(ko),
+                                  len(ko) - 1 if ko else 1, i32(local), u8(rec), u8(valid), cache_o, cache_lse,
+                                  out, lse, 0.0, None, delta, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(cache_lse=None), -1), (dict(rec=None), -1),
+    (dict(qo=None), -1), (dict(ko=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(S_q=-1), -2),
+    (dict(D=96), -7), (dict(D=256), -7),
+    (dict(qo=(0, 4, 4, 8)), -3), (dict(qo=(1, 8)), -3), (dict(qo=(0, 7)), -3),
+    (dict(ko=(0, 5, 4, 8)), -3), (dict(ko=(0, 4, 9)), -3),
+    (dict(rec=(2, 0)), -4), (dict(rec=(0, 1)), -4), (dict(local=(2,)), -4),
+    (dict(valid=(1, 0)), -5),
+    (dict(delta=1), -6), (dict(delta=1, ws=1, ws_bytes=4), -6),
+    (dict(delta=1, ws=1, ws_bytes=1 << 20, valid=(0, 1), rec=(1, 1)), -5),
+    (dict(delta=1, ws=1, ws_bytes=1 << 20, local=None), -1),
+])
+def test_validation_rejects_before_launch(L, kw, code):
+    assert _call(L, **kw) == code
+
+
+def test_too_many_blocks_or_partitions(L):
+    qo = list(range(0, 66))
+    assert _call(L, S_q=65, qo=qo, rec=[1, 0] * 65, local=[0] * 65) == -2
+    ko = list(range(0, 66))
+    assert _call(L, S_kv=65, ko=ko, rec=[1] + [0] * 64) == -2
+
+
+# ----------------------------------------------------------------------------- planner
+
+from partitioned_state_reuse_amd.api import Planner, DitError  # noqa: E402
+from oracle import RefPlanner  # noqa: E402
+
+
+def test_planner_rejects_bad_arguments(L):
+    with pytest.raises(DitError):
+        Planner(1, 4, [0, 2, 2, 4], [0], 5, 1, "wdelta")   # empty group
+    with pytest.raises(DitError):
+        Planner(1, 4, [0, 2, 4], [4], 5, 1, "wdelta")      # local out of range
+    with pytest.raises(DitError):
+        Planner(1, 4, [0, 2, 4], [0], 5, 3, "wdelta")      # K > G
+    with pytest.raises(DitError):
+        Planner(1, 4, [0, 2, 4], [0], 0, 1, "wdelta")      # no anchor period
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_planner_matches_oracle_planner_bit_exact(L, seed):
+    """Same (w, delta) inputs -> identical scores (bitwise) and identical selections."""
+    rng = np.random.default_rng(100 + seed)
+    P = int(rng.choice([8, 16, 32]))
+    gs = int(rng.choice([1, 2, 4]))
+    n_qb = int(rng.integers(1, 9))
+    go = list(range(0, P + 1, gs))
+    G = len(go) - 1
+    K = int(rng.integers(1, G + 1))
+    local = rng.integers(0, P, size=n_qb).tolist()
+    anchor_every = int(rng.integers(2, 6))
+    cp = Planner(n_qb, P, go, local, anchor_every, K, "wdelta")
+    rp = RefPlanner(n_qb, P, go, local, anchor_every, K, "wdelta")
+    for t in range(14):
+        sc, sr = cp.scores(t), np.array(rp.scores(t))
+        assert np.array_equal(sc, sr), (t, sc, sr)
+        m1, c1 = cp.next(t)
+        m2, c2 = rp.next(t)
+        assert np.array_equal(m1, m2) and c1 == c2, t
+        imp = None
+        if t % anchor_every == 0:
+            imp = rng.random((n_qb, P)).astype(np.float32)
+            if seed % 2:  # force exact ties
+                imp = np.round(imp * 4).astype(np.float32) / 4
+        d = rng.random(n_qb).astype(np.float32) * 0.1 if t > 0 else None
+        if d is not None and seed == 3:
+            d[0] = np.nan                                # unobserved entry
+        cp.observe(t, imp, d)
+        rp.observe(t, imp, d)
+    cp.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "video720p", "share32"])
+def test_distance_planner_matches_oracle(L, name):
+    import workloads as W
+    w = W.workload(name)
+    cp = Planner(w.n_qb, w.P, w.group_offsets, w.local_part, 0, w.recompute_groups, "distance")
+    rp = RefPlanner(w.n_qb, w.P, w.group_offsets, w.local_part, 0, w.recompute_groups, "distance")
+    m1, c1 = cp.next(0)
+    m2, c2 = rp.next(0)
+    assert np.array_equal(m1, m2) and c1 == c2
+
+
+def test_anchor_mode_all_ones(L):
+    cp = Planner(8, 8, list(range(9)), list(range(8)), 0, 8, "anchor")
+    m, _ = cp.next(3)
+    assert m.all()
