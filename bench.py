@@ -83,7 +83,33 @@ def cpu_baseline(w: W.Workload, X: "W.StepInputs", mask: np.ndarray, rows_per_bl
                       f"{w.P}-state merge; reused slots hold placeholder states"}
 
 
+def summarize_profile(db_path: str) -> str:
+    """Text summary of a rocprofv3 kernel trace (rocpd SQLite output): per kernel and grid
+    size, the dispatch count and the mean / min / max duration.  Grouping by grid separates
+    the cache-filling all-recompute dispatch from the timed steps' dispatches."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    rows = con.execute("select name, grid_x, grid_y, grid_z, workgroup_x, vgpr_count, accum_vgpr_count, "
+                       "lds_size, duration from kernels").fetchall()
+    groups = {}
+    for name, gx, gy, gz, wx, vg, ag, lds, dur in rows:
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        key = (short, gx, gy, gz, wx, vg, ag, lds)
+        groups.setdefault(key, []).append(dur)
+    lines = [f"{'kernel':<48} {'grid(x,y,z)':>22} {'wg':>4} {'vgpr':>5} {'agpr':>5} {'lds':>6} {'calls':>5} "
+             f"{'mean_us':>11} {'min_us':>11} {'max_us':>11}"]
+    for key, durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short, gx, gy, gz, wx, vg, ag, lds = key
+        d = np.array(durs, dtype=np.float64) / 1e3
+        lines.append(f"{short[:48]:<48} {f'{gx},{gy},{gz}':>22} {wx:>4} {vg:>5} {ag:>5} {lds:>6} {len(d):>5} "
+                     f"{d.mean():>11.2f} {d.min():>11.2f} {d.max():>11.2f}")
+    return "\n".join(lines)
+
+
 def main() -> int:
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profile":
+        print(summarize_profile(sys.argv[2]))
+        return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
