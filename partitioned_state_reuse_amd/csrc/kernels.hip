@@ -39,27 +39,85 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 //
 // One workgroup = 4 waves = one (batch, head, partition p, query tile of <= 128 rows of
 // one query block).  Each wave owns 32 query rows and keeps them in registers as the B
-// operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so that each lane's 16 scores
-// belong to one query and the softmax reductions over keys stay mostly inside a lane.
-// K tiles of 64 keys are staged in LDS row-major; V tiles are staged transposed (d-major)
-// so that V^T is the A operand of O^T = V^T P^T, with P^T taken straight from the score
-// registers (the key order inside each 16-key MFMA step is permuted identically on both
-// operands).  Online softmax in base 2 with fp32 state; P is rounded to bf16 for the
-// product.  The epilogue writes the partition's state into its cache slot and, for a
+// operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so that each lane's 16 scores per
+// 32-key block belong to one query and the softmax reductions over keys stay inside a
+// lane pair (l, l ^ 32), joined with v_permlane32_swap.
+//
+// K and V tiles of 64 keys are copied global -> LDS by the DMA path
+// (global_load_lds_dwordx4, no VGPR staging), double-buffered so that the next tile is in
+// flight while the current one is consumed.  Both tiles stay row-major [key][d] with a
+// per-row XOR swizzle of the 16-byte chunks, chosen so that the K reads (ds_read_b128, A
+// operand of K Q^T) and the V reads are free of bank conflicts.  V^T, the A operand of
+// O^T = V^T P^T, is read with the LDS transpose load ds_read_b64_tr_b16: in each group of
+// 16 lanes, lane i receives element i % 4 of the 8-byte chunks addressed by lanes
+// 4 j + i / 4, so pointing lane s of a group at V[key_(s / 4)][d0 + 4 (s % 4) ..] hands
+// every lane four keys of one d.  P^T, the B operand, comes straight from the score
+// registers; the key order inside each 16-key MFMA step is permuted identically on both
+// operands.
+//
+// Online softmax in base 2, fp32 state, with a lazy running maximum: the maximum used
+// for the exponentials is raised only when a tile's maximum exceeds it by more than
+// kRescaleLog2 (then exponentials stay <= 2^kRescaleLog2 and nothing overflows), which
+// skips the rescale of the accumulators on almost every tile.  P is rounded to bf16 for
+// the product.  The epilogue writes the partition's state into its cache slot and, for a
 // block's local partition, the partial sums of the local-change norm.
 // ------------------------------------------------------------------------------------
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D>
+struct TileGeom {
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int RPB = 256 / (2 * D);      // rows per 256 bytes (the 64 banks)
+  static constexpr int ROWS_PER_KB = 1024 / (2 * D);
+  static constexpr int TILE_ELEMS = kBlockN * D;
+  static constexpr int KB_PER_TILE = TILE_ELEMS * 2 / 1024;
+  static constexpr int KB_PER_WAVE = KB_PER_TILE / 4;
+  // physical chunk = logical chunk ^ swizzle(row)
+  static __device__ __forceinline__ int swz_k(int r) { return (r / RPB) % CPR; }
+  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 s16x4_lds;
+
+// One wave's share of the DMA copy of a 64-key tile (rows past `nvalid` re-read the last
+// valid row; their scores are masked and their V rows meet zero probabilities).
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_tile(const u16 *__restrict__ gtile, int rowstride, int nvalid,
+                                           u16 *lds_tile, int wave, int lane) {
+  using G = TileGeom<D>;
+#pragma unroll
+  for (int t = 0; t < G::KB_PER_WAVE; ++t) {
+    const int kb = wave * G::KB_PER_WAVE + t;
+    const int row = kb * G::ROWS_PER_KB + lane / G::CPR;
+    const int slot = lane % G::CPR;
+    const int c = slot ^ (IS_V ? G::swz_v(row) : G::swz_k(row));
+    const int src_row = min(row, nvalid - 1);
+    const u16 *src = gtile + (uint32_t)(src_row * rowstride + c * 8);
+    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(lds_tile + kb * 512), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ k, const u16 *__restrict__ v,
     u16 *__restrict__ cache_o, float *__restrict__ cache_lse, float *__restrict__ delta_part,
     const AttnDesc desc, const float scale_log2) {
+  using G = TileGeom<D>;
   constexpr int KK = D / 16;       // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
-  constexpr int KS = D + 8;        // LDS row stride (elements) of the K tile
-  constexpr int VS = kBlockN + 4;  // LDS row stride (elements) of the transposed V tile
-  __shared__ __attribute__((aligned(16))) u16 Ks[kBlockN * KS];
-  __shared__ __attribute__((aligned(16))) u16 Vt[D * VS];
-  __shared__ float red[8];
+  // [stage][K | V][64 x D]
+  __shared__ __attribute__((aligned(1024))) u16 lds[2][2][G::TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -97,7 +155,17 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
   const int qn = min(kBlockM, desc.q_off[blk + 1] - q0);
   const int kv0 = desc.kv_off[p];
   const int kvn = desc.kv_off[p + 1] - kv0;
-  const int64_t rowstride = (int64_t)H * D;
+  const int rowstride = H * D;
+  const int ntiles = (kvn + kBlockN - 1) / kBlockN;
+
+  const u16 *kbase = k + ((int64_t)b * desc.S_kv + kv0) * rowstride + (int64_t)head * D;
+  const u16 *vbase = v + ((int64_t)b * desc.S_kv + kv0) * rowstride + (int64_t)head * D;
+  const int64_t tile_step = (int64_t)kBlockN * rowstride;
+
+  if (ntiles > 0) {
+    issue_tile<D, false>(kbase, rowstride, kvn, lds[0][0], wave, lane);
+    issue_tile<D, true>(vbase, rowstride, kvn, lds[0][1], wave, lane);
+  }
 
   // ---- this lane's query row, as the B operand: Q[row][16 kk + 8 hh + 0..7]
   const int qrow = wave * 32 + l32;
@@ -114,118 +182,96 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
     }
   }
 
+  // ---- per-lane LDS element offsets (the swizzle depends only on the lane)
+  int koff[KK];
+  {
+    const int x = hh ^ G::swz_k(l32);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) koff[kk] = l32 * D + ((2 * kk) ^ x) * 8;
+  }
+  int voff[DB];
+  {
+    const int grp = lane >> 4, ls = lane & 15;
+    const int vrow = 4 * (grp >> 1) + (ls >> 2);
+    const int sv = G::swz_v(vrow);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int cidx = 4 * db + 2 * (grp & 1) + ((ls & 3) >> 1);
+      voff[db] = vrow * D + (cidx ^ sv) * 8 + (ls & 1) * 4;
+    }
+  }
+
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
-
-  const u16 *kbase = k + ((int64_t)b * desc.S_kv + kv0) * rowstride + (int64_t)head * D;
-  const u16 *vbase = v + ((int64_t)b * desc.S_kv + kv0) * rowstride + (int64_t)head * D;
-  const int ntiles = (kvn + kBlockN - 1) / kBlockN;
+  float m = -INFINITY, lsum = 0.f;   // m: running maximum in scaled base-2 units
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int key0 = kt * kBlockN;
-    const int nvalid = min(kBlockN, kvn - key0);
-    // ---- stage K rows [key][d]; rows past the partition end are zero
-    {
-      constexpr int CPR = D / 8;
-      constexpr int RPP = 256 / CPR;
-      const int c = tid % CPR;
-#pragma unroll
-      for (int pass = 0; pass < kBlockN / RPP; ++pass) {
-        const int r = tid / CPR + pass * RPP;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (r < nvalid) val = *(const uint4 *)(kbase + (int64_t)(key0 + r) * rowstride + 8 * c);
-        *(uint4 *)(Ks + r * KS + 8 * c) = val;
-      }
-    }
-    // ---- stage V transposed [d][key]: each thread loads KPT consecutive keys of one
-    // 8-wide d chunk and writes, per d, their KPT values as one LDS store
-    {
-      constexpr int KPT = D / 32;
-      constexpr int KG = kBlockN / KPT;
-      const int kg = tid % KG;
-      const int dc = tid / KG;
-      uint4 val[KPT];
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int key = kg * KPT + j;
-        val[j] = make_uint4(0, 0, 0, 0);
-        if (key < nvalid) val[j] = *(const uint4 *)(vbase + (int64_t)(key0 + key) * rowstride + 8 * dc);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t w[KPT / 2];
-#pragma unroll
-        for (int j2 = 0; j2 < KPT / 2; ++j2) {
-          const uint32_t a0 = ((const uint32_t *)&val[2 * j2])[e >> 1];
-          const uint32_t a1 = ((const uint32_t *)&val[2 * j2 + 1])[e >> 1];
-          const uint32_t lo = (e & 1) ? (a0 >> 16) : (a0 & 0xffffu);
-          const uint32_t hi = (e & 1) ? (a1 >> 16) : (a1 & 0xffffu);
-          w[j2] = lo | (hi << 16);
-        }
-        u16 *dst = Vt + (8 * dc + e) * VS + kg * KPT;
-        if constexpr (KPT == 4) {
-          *(uint2 *)dst = make_uint2(w[0], w[1]);
-        } else {
-          *(uint32_t *)dst = w[0];
-        }
-      }
-    }
+    const int stage = kt & 1;
+    // the tile landed: own DMA complete, then everyone's
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    if (kt + 1 < ntiles) {
+      const int nv = min(kBlockN, kvn - (kt + 1) * kBlockN);
+      issue_tile<D, false>(kbase + (kt + 1) * tile_step, rowstride, nv, lds[stage ^ 1][0], wave, lane);
+      issue_tile<D, true>(vbase + (kt + 1) * tile_step, rowstride, nv, lds[stage ^ 1][1], wave, lane);
+    }
+    const u16 *Kt = lds[stage][0];
+    const u16 *Vt = lds[stage][1];
+    const int nvalid = min(kBlockN, kvn - kt * kBlockN);
 
     // ---- S^T = K Q^T for keys [32 mb, 32 mb + 32)
     f32x16 s[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 a = as_bf16x8(*(const uint4 *)(Ks + (32 * mb + l32) * KS + 16 * kk + 8 * hh));
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a = as_bf16x8(*(const uint4 *)(Kt + koff[kk] + mb * 32 * D));
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
       }
     }
 
-    // ---- scale into base 2; mask keys past the partition end.  s[mb][r] holds key
+    // ---- mask keys past the partition end.  s[mb][r] holds key
     // 32 mb + (r & 3) + 8 (r >> 2) + 4 hh of the tile for query row l32.
-    if (nvalid == kBlockN) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mb][r] *= scale_log2;
-    } else {
+    if (nvalid < kBlockN) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * mb + (r & 3) + 8 * (r >> 2) + 4 * hh;
-          s[mb][r] = key < nvalid ? s[mb][r] * scale_log2 : -INFINITY;
+          if (key >= nvalid) s[mb][r] = -INFINITY;
         }
     }
 
     // ---- online softmax: the lane pair (l, l ^ 32) holds all 64 keys of one query
-    float mt = s[0][0];
+    float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[mb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
-    lsum *= alpha;
+      for (int r = (mb == 0 ? 2 : 0); r < 16; ++r) mt = fmaxf(mt, s[mb][r]);
+    mt = pair_max(mt) * scale_log2;
+    if (__ballot(mt > m + kRescaleLog2)) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      lsum *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    const float negm = -m;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(s[mb][r] - mnew);
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], scale_log2, negm));
         s[mb][r] = e;
         lsum += e;
       }
@@ -244,18 +290,19 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
       const bf16x8 pb = as_bf16x8(pu);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u16 *vp = Vt + (32 * db + l32) * VS + 16 * c + 4 * hh;
-        const uint2 lo = *(const uint2 *)vp;
-        const uint2 hi = *(const uint2 *)(vp + 8);
-        const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const u16 *vp = Vt + voff[db] + 16 * c * D;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds *)(vp));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds *)(vp + 8 * D));
+        const uint2 lo2 = __builtin_bit_cast(uint2, lo);
+        const uint2 hi2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8 a = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
 
   // ---- epilogue: normalise, write the state into cache slot (p, rows), local change
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = pair_sum(lsum);
   const bool empty = !(ltot > 0.f);
   const float inv = empty ? 0.f : 1.f / ltot;
   const float lse_nat = empty ? -INFINITY : (m + __log2f(ltot)) * kLn2;
@@ -294,6 +341,8 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
       dnum += __shfl_xor(dnum, off);
       dden += __shfl_xor(dden, off);
     }
+    float *red = (float *)&lds[0][0][0];
+    __syncthreads();  // every wave is done with the tiles before the scratch is reused
     if (lane == 0) {
       red[2 * wave] = dnum;
       red[2 * wave + 1] = dden;
