@@ -7,6 +7,8 @@
 // (O_p, lse_p) is produced; the states are composed by LSE-weighted combination.
 #include <math.h>
 
+#include <type_traits>
+
 #include "launch.h"
 
 namespace dit {
@@ -37,8 +39,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // ------------------------------------------------------------------------------------
 // Partition attention.
 //
-// One workgroup = 4 waves = one (batch, head, partition p, query tile of <= 128 rows of
-// one query block).  Each wave owns 32 query rows and keeps them in registers as the B
+// One workgroup = 8 waves (two per SIMD) = one (batch, head, partition p, query tile of
+// <= 256 rows of one query block); a wave whose 32 rows all lie past the block end only
+// helps with the tile copies.  Each wave owns 32 query rows and keeps them in registers as the B
 // operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so that each lane's 16 scores per
 // 32-key block belong to one query and the softmax reductions over keys stay inside a
 // lane pair (l, l ^ 32), joined with v_permlane32_swap.
@@ -71,7 +74,8 @@ struct TileGeom {
   static constexpr int ROWS_PER_KB = 1024 / (2 * D);
   static constexpr int TILE_ELEMS = kBlockN * D;
   static constexpr int KB_PER_TILE = TILE_ELEMS * 2 / 1024;
-  static constexpr int KB_PER_WAVE = KB_PER_TILE / 4;
+  // waves past KB_PER_TILE issue nothing when a tile has fewer 1-KB blocks than waves
+  static constexpr int KB_PER_WAVE = (KB_PER_TILE + kWaves - 1) / kWaves;
   // physical chunk = logical chunk ^ swizzle(row)
   static __device__ __forceinline__ int swz_k(int r) { return (r / RPB) % CPR; }
   static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
@@ -81,21 +85,36 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 s16x4_lds;
 
-// One wave's share of the DMA copy of a 64-key tile (rows past `nvalid` re-read the last
-// valid row; their scores are masked and their V rows meet zero probabilities).
+// Per-lane byte offsets (within a tile of one head) of this lane's share of the DMA copy:
+// for each of the wave's 1-KB destination blocks, the lane fills physical chunk
+// `lane % CPR` of row `kb * ROWS_PER_KB + lane / CPR`, which holds logical chunk
+// `slot ^ swizzle(row)`.  Rows at or past `nvalid` re-read row nvalid - 1 (their scores
+// are masked and their V rows meet zero probabilities), so no load leaves the partition.
 template <int D, bool IS_V>
-__device__ __forceinline__ void issue_tile(const u16 *__restrict__ gtile, int rowstride, int nvalid,
-                                           u16 *lds_tile, int wave, int lane) {
+__device__ __forceinline__ void dma_offsets(int rowstride, int nvalid, int wave, int lane,
+                                            uint32_t (&off)[TileGeom<D>::KB_PER_WAVE]) {
   using G = TileGeom<D>;
 #pragma unroll
   for (int t = 0; t < G::KB_PER_WAVE; ++t) {
     const int kb = wave * G::KB_PER_WAVE + t;
-    const int row = kb * G::ROWS_PER_KB + lane / G::CPR;
-    const int slot = lane % G::CPR;
-    const int c = slot ^ (IS_V ? G::swz_v(row) : G::swz_k(row));
-    const int src_row = min(row, nvalid - 1);
-    const u16 *src = gtile + (uint32_t)(src_row * rowstride + c * 8);
-    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(lds_tile + kb * 512), 16, 0, 0);
+    const int row = min(kb, G::KB_PER_TILE - 1) * G::ROWS_PER_KB + lane / G::CPR;
+    const int c = (lane % G::CPR) ^ (IS_V ? G::swz_v(row) : G::swz_k(row));
+    off[t] = (uint32_t)(min(row, nvalid - 1) * rowstride + c * 8) * 2u;
+  }
+}
+
+// Issue one wave's share of the DMA copy of a tile (tile base and wave index are uniform).
+template <int D>
+__device__ __forceinline__ void issue_tile(const u16 *__restrict__ gtile,
+                                           const uint32_t (&off)[TileGeom<D>::KB_PER_WAVE],
+                                           u16 *lds_tile, int wave) {
+  using G = TileGeom<D>;
+#pragma unroll
+  for (int t = 0; t < G::KB_PER_WAVE; ++t) {
+    const int kb = wave * G::KB_PER_WAVE + t;
+    if (G::KB_PER_TILE % kWaves == 0 || kb < G::KB_PER_TILE)
+      __builtin_amdgcn_global_load_lds((const void *)((const char *)gtile + off[t]),
+                                       (lds_void *)(lds_tile + kb * 512), 16, 0, 0);
   }
 }
 
@@ -109,15 +128,21 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void partition_attention_kernel(
+__global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ k, const u16 *__restrict__ v,
     u16 *__restrict__ cache_o, float *__restrict__ cache_lse, float *__restrict__ delta_part,
     const AttnDesc desc, const float scale_log2) {
   using G = TileGeom<D>;
-  constexpr int KK = D / 16;       // k-steps of S^T = K Q^T
-  constexpr int DB = D / 32;       // 32-row blocks of O^T
-  // [stage][K | V][64 x D]
-  __shared__ __attribute__((aligned(1024))) u16 lds[2][2][G::TILE_ELEMS];
+  constexpr int KK = D / 16;        // k-steps of S^T = K Q^T
+  constexpr int DB = D / 32;        // 32-row blocks of O^T
+  constexpr int MB = kBlockN / 32;  // 32-key blocks of S^T per tile
+  constexpr int NC = kBlockN / 16;  // 16-key steps of O^T += V^T P^T per tile
+  // K and V tiles, two of each; separate variables so that the compiler knows a DMA into
+  // one buffer does not alias reads of another (no wait is inserted for it)
+  __shared__ __attribute__((aligned(1024))) u16 k_lds0[G::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) u16 k_lds1[G::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) u16 v_lds0[G::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) u16 v_lds1[G::TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,14 +187,46 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
   const u16 *vbase = v + ((int64_t)b * desc.S_kv + kv0) * rowstride + (int64_t)head * D;
   const int64_t tile_step = (int64_t)kBlockN * rowstride;
 
+  // ---- DMA offsets of full tiles; the last tile's clamped ones are made when it is issued
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int last_valid = kvn - (ntiles - 1) * kBlockN;
+  uint32_t koff_full[G::KB_PER_WAVE], voff_full[G::KB_PER_WAVE];
+  dma_offsets<D, false>(rowstride, kBlockN, wave_u, lane, koff_full);
+  dma_offsets<D, true>(rowstride, kBlockN, wave_u, lane, voff_full);
+  // Buffer parity is a compile-time argument everywhere: k_lds<t & 1> holds K tile t and
+  // v_lds<t & 1> holds V tile t.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  auto kbuf = [&](auto par) -> u16 * { if constexpr (decltype(par)::value) return k_lds1; else return k_lds0; };
+  auto vbuf = [&](auto par) -> u16 * { if constexpr (decltype(par)::value) return v_lds1; else return v_lds0; };
+  auto issue_k = [&](int t, auto par) {
+    if (t == ntiles - 1 && last_valid < kBlockN) {
+      uint32_t off[G::KB_PER_WAVE];
+      dma_offsets<D, false>(rowstride, last_valid, wave_u, lane, off);
+      issue_tile<D>(kbase + t * tile_step, off, kbuf(par), wave_u);
+    } else {
+      issue_tile<D>(kbase + t * tile_step, koff_full, kbuf(par), wave_u);
+    }
+  };
+  auto issue_v = [&](int t, auto par) {
+    if (t == ntiles - 1 && last_valid < kBlockN) {
+      uint32_t off[G::KB_PER_WAVE];
+      dma_offsets<D, true>(rowstride, last_valid, wave_u, lane, off);
+      issue_tile<D>(vbase + t * tile_step, off, vbuf(par), wave_u);
+    } else {
+      issue_tile<D>(vbase + t * tile_step, voff_full, vbuf(par), wave_u);
+    }
+  };
   if (ntiles > 0) {
-    issue_tile<D, false>(kbase, rowstride, kvn, lds[0][0], wave, lane);
-    issue_tile<D, true>(vbase, rowstride, kvn, lds[0][1], wave, lane);
+    issue_k(0, P0{});
+    issue_v(0, P0{});
+    if (kPipeline && ntiles > 1) issue_k(1, P1{});
   }
 
   // ---- this lane's query row, as the B operand: Q[row][16 kk + 8 hh + 0..7]
   const int qrow = wave * 32 + l32;
   const bool qvalid = qrow < qn;
+  const bool active = wave * 32 < qn;  // wave-uniform: some of this wave's rows exist
   bf16x8 qf[KK];
   {
     const u16 *qp = q + ((int64_t)b * desc.S_q + q0 + (qvalid ? qrow : 0)) * rowstride +
@@ -182,23 +239,19 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
     }
   }
 
-  // ---- per-lane LDS element offsets (the swizzle depends only on the lane)
-  int koff[KK];
+  // ---- per-lane LDS byte offsets of the MFMA operand reads.  The XOR swizzle acts on
+  // address bits below the row base, so each k-step (K) or d-block (V) is one XOR away
+  // from the lane's base offset: K step kk at k_lane ^ (kk << 5), V d-block db at
+  // v_lane ^ (db << 6).
+  uint32_t k_lane, v_lane;
   {
     const int x = hh ^ G::swz_k(l32);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) koff[kk] = l32 * D + ((2 * kk) ^ x) * 8;
-  }
-  int voff[DB];
-  {
+    k_lane = (uint32_t)(l32 * D + x * 8) * 2u;
     const int grp = lane >> 4, ls = lane & 15;
     const int vrow = 4 * (grp >> 1) + (ls >> 2);
     const int sv = G::swz_v(vrow);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int cidx = 4 * db + 2 * (grp & 1) + ((ls & 3) >> 1);
-      voff[db] = vrow * D + (cidx ^ sv) * 8 + (ls & 1) * 4;
-    }
+    const int cidx0 = 2 * (grp & 1) + ((ls & 3) >> 1);
+    v_lane = (uint32_t)(vrow * D + (cidx0 ^ sv) * 8 + (ls & 1) * 4) * 2u;
   }
 
   f32x16 o[DB];
@@ -208,54 +261,45 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m = -INFINITY, lsum = 0.f;   // m: running maximum in scaled base-2 units
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int stage = kt & 1;
-    // the tile landed: own DMA complete, then everyone's
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (kt + 1 < ntiles) {
-      const int nv = min(kBlockN, kvn - (kt + 1) * kBlockN);
-      issue_tile<D, false>(kbase + (kt + 1) * tile_step, rowstride, nv, lds[stage ^ 1][0], wave, lane);
-      issue_tile<D, true>(vbase + (kt + 1) * tile_step, rowstride, nv, lds[stage ^ 1][1], wave, lane);
-    }
-    const u16 *Kt = lds[stage][0];
-    const u16 *Vt = lds[stage][1];
-    const int nvalid = min(kBlockN, kvn - kt * kBlockN);
-
-    // ---- S^T = K Q^T for keys [32 mb, 32 mb + 32)
-    f32x16 s[2];
+  // S^T = K Q^T of the K tile in `Kt`: s[mb][r] holds key 32 mb + (r & 3) + 8 (r >> 2) + 4 hh
+  // of the tile for query row l32.
+  auto qk = [&](const u16 *Kt, f32x16 (&s)[MB]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = as_bf16x8(*(const uint4 *)(Kt + koff[kk] + mb * 32 * D));
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 a = as_bf16x8(*(const uint4 *)((const char *)Kt + (k_lane ^ (uint32_t)(kk << 5)) + mb * 64 * D));
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
       }
     }
-
-    // ---- mask keys past the partition end.  s[mb][r] holds key
-    // 32 mb + (r & 3) + 8 (r >> 2) + 4 hh of the tile for query row l32.
-    if (nvalid < kBlockN) {
+  };
+  // Keys at or past `nvalid` of the tile get score -inf.
+  auto mask_tail = [&](f32x16 (&s)[MB], int nvalid) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * mb + (r & 3) + 8 * (r >> 2) + 4 * hh;
-          if (key >= nvalid) s[mb][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax: the lane pair (l, l ^ 32) holds all 64 keys of one query
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * mb + (r & 3) + 8 * (r >> 2) + 4 * hh;
+        if (key >= nvalid) s[mb][r] = -INFINITY;
+      }
+  };
+  // Maximum of a tile's scores for this lane's query (the lane pair holds all keys of the
+  // tile), in scaled base-2 units.
+  auto tile_max = [&](const f32x16 (&s)[MB]) {
     float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = (mb == 0 ? 2 : 0); r < 16; ++r) mt = fmaxf(mt, s[mb][r]);
-    mt = pair_max(mt) * scale_log2;
+    return pair_max(mt) * scale_log2;
+  };
+  // Lazy running maximum: raise it (and rescale the accumulators) only when the tile's
+  // maximum exceeds it by more than kRescaleLog2 for some lane of the wave.
+  auto rescale = [&](float mt) {
     if (__ballot(mt > m + kRescaleLog2)) {
       const float mnew = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -266,38 +310,131 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
+  };
+  // Probabilities of a tile, summed into lsum and packed to bf16 as the B operand of the
+  // 16-key PV steps.
+  auto probs = [&](const f32x16 (&s)[MB], bf16x8 (&pb)[NC]) {
     const float negm = -m;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], scale_log2, negm));
-        s[mb][r] = e;
-        lsum += e;
-      }
-
-    // ---- O^T += V^T P^T over four 16-key steps.  k-index 8 hh + j of step c stands for
-    // key 16 c + 4 hh + 8 (j >> 2) + (j & 3) on both operands.
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const int mb = c >> 1;
       const int base = 8 * (c & 1);
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][base + j], scale_log2, negm));
+        lsum += e[j];
+      }
       uint4 pu;
-      pu.x = pack_bf16x2(s[mb][base + 0], s[mb][base + 1]);
-      pu.y = pack_bf16x2(s[mb][base + 2], s[mb][base + 3]);
-      pu.z = pack_bf16x2(s[mb][base + 4], s[mb][base + 5]);
-      pu.w = pack_bf16x2(s[mb][base + 6], s[mb][base + 7]);
-      const bf16x8 pb = as_bf16x8(pu);
+      pu.x = pack_bf16x2(e[0], e[1]);
+      pu.y = pack_bf16x2(e[2], e[3]);
+      pu.z = pack_bf16x2(e[4], e[5]);
+      pu.w = pack_bf16x2(e[6], e[7]);
+      pb[c] = as_bf16x8(pu);
+    }
+  };
+  // O^T += V^T P^T over the 16-key steps.  k-index 8 hh + j of step c stands for key
+  // 16 c + 4 hh + 8 (j >> 2) + (j & 3) on both operands.
+  auto pv = [&](const u16 *Vt, const bf16x8 (&pb)[NC]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u16 *vp = Vt + voff[db] + 16 * c * D;
+        const u16 *vp = (const u16 *)((const char *)Vt + (v_lane ^ (uint32_t)(db << 6)) + 32 * c * D);
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds *)(vp));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds *)(vp + 8 * D));
         const uint2 lo2 = __builtin_bit_cast(uint2, lo);
         const uint2 hi2 = __builtin_bit_cast(uint2, hi);
         const bf16x8 a = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], o[db], 0, 0, 0);
       }
+    }
+  };
+  auto wait_tiles = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
+    __syncthreads();                     // ... and every wave's, and all reads of the old buffers are done
+  };
+
+  if constexpr (kPipeline) {
+    // K runs one tile ahead of V.  Step kt (parity PAR of tile kt): tile kt+1's K Q^T MFMAs
+    // overlap tile kt's exponentials, and tile kt's V^T P^T MFMAs overlap tile kt+1's
+    // maximum.  On entry `cur` holds tile kt's scores and `mt_cur` their maximum; on exit
+    // they hold tile kt+1's.
+    auto step = [&](int kt, auto par, f32x16 (&cur)[MB], float &mt_cur) {
+      constexpr int PAR = decltype(par)::value;
+      using Pn = std::integral_constant<int, PAR ^ 1>;
+      if (kt + 2 < ntiles) issue_k(kt + 2, par);
+      issue_v(kt + 1, Pn{});
+      if (active) {
+        rescale(mt_cur);
+        bf16x8 pb[NC];
+        f32x16 nxt[MB];
+        qk(kbuf(Pn{}), nxt);
+        probs(cur, pb);
+        if (kt + 1 == ntiles - 1 && last_valid < kBlockN) mask_tail(nxt, last_valid);
+        pv(vbuf(par), pb);
+        mt_cur = tile_max(nxt);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) cur[mb] = nxt[mb];
+      }
+      wait_tiles();
+    };
+    auto last_step = [&](auto par, const f32x16 (&cur)[MB], float mt_cur) {
+      if (!active) return;
+      rescale(mt_cur);
+      bf16x8 pb[NC];
+      probs(cur, pb);
+      pv(vbuf(par), pb);
+    };
+    if (ntiles > 0) {
+      wait_tiles();
+      f32x16 cur[MB];
+      float mt_cur = 0.f;
+      if (active) {
+        qk(k_lds0, cur);
+        if (ntiles == 1 && last_valid < kBlockN) mask_tail(cur, last_valid);
+        mt_cur = tile_max(cur);
+      }
+      int kt = 0;
+      for (; kt + 2 < ntiles; kt += 2) {
+        step(kt, P0{}, cur, mt_cur);
+        step(kt + 1, P1{}, cur, mt_cur);
+      }
+      if (kt + 1 < ntiles) {
+        step(kt, P0{}, cur, mt_cur);
+        last_step(P1{}, cur, mt_cur);
+      } else {
+        last_step(P0{}, cur, mt_cur);
+      }
+    }
+  } else {
+    // K and V of tile kt+1 are copied while tile kt is consumed.
+    auto step = [&](int kt, auto par) {
+      constexpr int PAR = decltype(par)::value;
+      using Pn = std::integral_constant<int, PAR ^ 1>;
+      if (kt + 1 < ntiles) {
+        issue_k(kt + 1, Pn{});
+        issue_v(kt + 1, Pn{});
+      }
+      if (active) {
+        f32x16 s[MB];
+        qk(kbuf(par), s);
+        if (kt == ntiles - 1 && last_valid < kBlockN) mask_tail(s, last_valid);
+        rescale(tile_max(s));
+        bf16x8 pb[NC];
+        probs(s, pb);
+        pv(vbuf(par), pb);
+      }
+      wait_tiles();
+    };
+    if (ntiles > 0) {
+      wait_tiles();
+      int kt = 0;
+      for (; kt + 1 < ntiles; kt += 2) {
+        step(kt, P0{});
+        step(kt + 1, P1{});
+      }
+      if (kt < ntiles) step(kt, P0{});
     }
   }
 
@@ -341,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
       dnum += __shfl_xor(dnum, off);
       dden += __shfl_xor(dden, off);
     }
-    float *red = (float *)&lds[0][0][0];
+    float *red = (float *)k_lds0;
     __syncthreads();  // every wave is done with the tiles before the scratch is reused
     if (lane == 0) {
       red[2 * wave] = dnum;
@@ -349,8 +486,11 @@ __global__ __launch_bounds__(256, 2) void partition_attention_kernel(
     }
     __syncthreads();
     if (tid == 0) {
-      const float n = ((red[0] + red[2]) + red[4]) + red[6];
-      const float d = ((red[1] + red[3]) + red[5]) + red[7];
+      float n = 0.f, d = 0.f;
+      for (int w = 0; w < kWaves; ++w) {
+        n += red[2 * w];
+        d += red[2 * w + 1];
+      }
       float *dp = delta_part + (((int64_t)b * desc.n_tiles + desc.tile_prefix[blk] + tile) * H + head) * 2;
       dp[0] = n;
       dp[1] = d;
@@ -507,7 +647,7 @@ hipError_t launch_partition_attention(int D, const void *q, const void *k, const
   const int64_t nwg = (int64_t)desc.B * desc.H * desc.items_per_head;
   if (nwg == 0) return hipSuccess;
   (void)hipGetLastError();
-  dim3 grid((unsigned)nwg), block(256);
+  dim3 grid((unsigned)nwg), block(kWaves * 64);
   if (D == 128)
     hipLaunchKernelGGL(partition_attention_kernel<128>, grid, block, 0, stream, (const u16 *)q,
                        (const u16 *)k, (const u16 *)v, (u16 *)cache_o, cache_lse, delta_partials, desc,

@@ -8,8 +8,24 @@
 
 namespace dit {
 
-constexpr int kBlockM = 128;  // query rows per attention workgroup (4 waves x 32 rows)
-constexpr int kBlockN = 64;   // keys per staged KV tile
+// Partition-attention tile shape (build-time parameters).
+#ifndef DIT_ATTN_WAVES
+#define DIT_ATTN_WAVES 4
+#endif
+#ifndef DIT_ATTN_BLOCK_N
+#define DIT_ATTN_BLOCK_N 32
+#endif
+#ifndef DIT_ATTN_PIPELINE
+#define DIT_ATTN_PIPELINE 0
+#endif
+#ifndef DIT_ATTN_MIN_BLOCKS
+#define DIT_ATTN_MIN_BLOCKS 3
+#endif
+constexpr int kWaves = DIT_ATTN_WAVES;      // waves per attention workgroup
+constexpr int kBlockM = 32 * kWaves;        // query rows per attention workgroup (32 per wave)
+constexpr int kBlockN = DIT_ATTN_BLOCK_N;   // keys per staged KV tile (32 or 64)
+constexpr bool kPipeline = DIT_ATTN_PIPELINE != 0;  // overlap tile j+1's K Q^T with tile j's softmax
+constexpr int kMinBlocks = DIT_ATTN_MIN_BLOCKS;     // attention workgroups resident per CU (register budget)
 
 // Work description of one partition-attention launch, passed by value as a kernel
 // argument so that a launch needs no host-to-device copy.

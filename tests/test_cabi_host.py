@@ -45,7 +45,7 @@ def test_status_strings(L):
 
 
 def test_workspace_bytes(L):
-    assert L.dit_attn_workspace_bytes(1, 75600, 40, 128, 16, 16) == (591 + 16) * 40 * 8
+    assert L.dit_attn_workspace_bytes(1, 75600, 40, 128, 16, 16) == (591 + 16) * 40 * 8  # 128-row query tiles
     assert L.dit_attn_workspace_bytes(1, 100, 4, 96, 1, 1) == 0      # unsupported D
     assert L.dit_attn_workspace_bytes(1, 100, 4, 64, 0, 1) == 0      # no blocks
     assert L.dit_attn_workspace_bytes(1, 100, 4, 64, 1, 65) == 0     # too many partitions
