@@ -499,9 +499,11 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
 }
 
 // ------------------------------------------------------------------------------------
-// State merge: one thread per 8 consecutive d of one (row, head); all P lse values of the
-// row-head are kept in registers (PMAX >= P, unrolled), then the P bf16 states are
-// streamed with 16-byte loads and combined in fp32.
+// State merge: one thread per 8 consecutive d of one (row, head), a workgroup per 16
+// consecutive row-heads (4 KB contiguous runs of every partition plane); all P lse values
+// of the row-head are kept in registers (PMAX >= P, unrolled), then the P bf16 states are
+// streamed with 16-byte non-temporal loads and combined in fp32; the merged output is
+// written with non-temporal stores (it is not re-read by this step).
 // ------------------------------------------------------------------------------------
 template <int D, int PMAX>
 __global__ __launch_bounds__(256) void state_merge_kernel(
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(256) void state_merge_kernel(
   res.y = pack_bf16x2(acc[2], acc[3]);
   res.z = pack_bf16x2(acc[4], acc[5]);
   res.w = pack_bf16x2(acc[6], acc[7]);
-  *(uint4 *)(out + rh * D + 8 * c) = res;
+  __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
   if (c == 0) lse_out[li] = L;
 }
 
