@@ -326,6 +326,22 @@ def make_tensor(w: Workload, which: int, step: int = 0, token_range: Optional[Tu
     return bits[None]
 
 
+def trajectory(w: Workload, token_ranges=None):
+    """Yield (t, StepInputs) for t = 0 .. w.steps - 1 of a drifting trajectory, keeping the
+    pre-RoPE float32 running values (X_t = X_{t-1} + drift_scale * N_t), so that each step
+    costs one draw per tensor.  `token_ranges` optionally restricts (q, k, v) tokens."""
+    rng_q, rng_k, rng_v = token_ranges or (w.q_token_range, (0, w.S_kv), (0, w.S_kv))
+    ranges = [rng_q, rng_k, rng_v]
+    cur = [base_f32(w, which, *ranges[which]) for which in (T_Q, T_K, T_V)]
+    for t in range(w.steps):
+        if t > 0:
+            for which in (T_Q, T_K, T_V):
+                n = normal_tokens(w.seed, noise_id(t, which), *ranges[which], w.H, w.D)
+                cur[which] = cur[which] + np.float32(w.drift_scale) * n
+        bits = [_finish(w, cur[which], *ranges[which], rope=(which != T_V))[None] for which in (T_Q, T_K, T_V)]
+        yield t, StepInputs(q=bits[0], k=bits[1], v=bits[2])
+
+
 def make_step(w: Workload, step: int = 0) -> StepInputs:
     return StepInputs(q=make_tensor(w, T_Q, step), k=make_tensor(w, T_K, step), v=make_tensor(w, T_V, step))
 
