@@ -142,12 +142,50 @@ int dit_partition_attention(const void *q, const void *k, const void *v,
  * State merge: for every query row and head, compose the P cached states (all P slots,
  * as the partition-attention call left them) into out / lse by LSE-weighted combination in
  * fp32; states with lse = -inf carry no weight; if every state is empty, out = 0 and
- * lse = -inf.  n_qb/q_offsets are accepted for validation symmetry and may be 1 / NULL.
+ * lse = -inf.
  */
 int dit_state_merge(const void *cache_o, const float *cache_lse,
                     int B, int S_q, int H, int D, int P,
                     void *out, float *lse,
                     void *stream);
+
+/*
+ * Masked state merge: like dit_state_merge, but row r of query block i composes only the
+ * cache planes p with plane_select[i * P + p] = 1 (host [n_qb * P], values 0/1), plus the
+ * extra state (extra_o [B, S_q, H, D] bf16, extra_lse [B, H, S_q] f32) when both pointers
+ * are non-NULL.  With nothing selected and no extra state, out = 0 and lse = -inf.
+ * This is the one-GPU form of filling compute bubbles with reuse work ("Methodology §2,
+ * Pipeline Orchestration"): the reused states can be pre-merged into a partial state on a
+ * second stream while dit_partition_attention writes the recomputed slots (disjoint memory),
+ * then the fresh states and the partial are merged.  out/lse may be the extra state itself
+ * only if they are not also read by another stream at the same time.
+ */
+int dit_state_merge_masked(const void *cache_o, const float *cache_lse,
+                           int B, int S_q, int H, int D, int P,
+                           const int32_t *q_offsets, int n_qb,
+                           const uint8_t *plane_select,
+                           const void *extra_o, const float *extra_lse,
+                           void *out, float *lse,
+                           void *stream);
+
+/*
+ * Dynamic group compose ("Methodology §2, Dynamic Group Compose"): compose the cached
+ * states of runs of adjacent partitions into coarser states, with no recomputation.
+ * Output plane g is the LSE-weighted combination of input planes
+ * group_offsets[g] .. group_offsets[g+1]-1 (same rule as dit_state_merge, fp32 math).
+ *   cache_o, cache_lse   device in: [P_in, B, S_q, H, D] bf16, [P_in, B, H, S_q] f32
+ *   group_offsets        host [G+1]: 0 = first, strictly increasing, last = P_in
+ *   out_o, out_lse       device out: [G, B, S_q, H, D] bf16, [G, B, H, S_q] f32; must not
+ *                        overlap the input planes
+ * Applying it again to its output coarsens further (composition is associative).  After
+ * composing, later steps run with the group offsets as partition offsets and the composed
+ * planes as the state cache.
+ */
+int dit_state_compose(const void *cache_o, const float *cache_lse, int P_in,
+                      const int32_t *group_offsets, int G,
+                      int B, int S_q, int H, int D,
+                      void *out_o, float *out_lse,
+                      void *stream);
 
 /*
  * Partition importance from the cached states and the merged lse of this step:

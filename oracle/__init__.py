@@ -15,8 +15,11 @@ Parity pins (see tests/test_oracle_pins.py and tests/test_oracle_planner.py):
   local_change                    - V_t = c V_{t-1} gives |c - 1|; unchanged gives 0
   RefPlanner                      - brute-force subset enumeration; round-robin closed
                                     form; hand-derived selection lists
+  compose_states                  - composed state == brute-force attention over the union
+                                    of the group's keys; merge after compose == merge;
+                                    recursive composition == one-shot composition
 """
-from .attention import (StateCache, StepResult, full_attention, importance, local_change,
+from .attention import (StateCache, StepResult, compose_states, full_attention, importance, local_change,
                         merge_states, merge_weights, partition_state, round_bf16, round_f32,
                         selective_step, block_of_rows)
 from .planner import RefPlanner, group_distance, group_of

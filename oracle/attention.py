@@ -181,6 +181,21 @@ def selective_step(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.nd
     return StepResult(O=O, lse=lse, O_stored=O_s, lse_stored=lse_s, weights=W, fresh_lse=fresh_lse)
 
 
+def compose_states(O: np.ndarray, lse: np.ndarray, group_offsets: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """Dynamic Group Compose (DiTango pages, "Methodology §2, Dynamic Group Compose"): the
+    cached states of each run of adjacent partitions [g_j, g_{j+1}) are composed into one
+    coarser state, with no recomputation.  O: [P, n, H, D], lse: [P, H, n] ->
+    [G, n, H, D], [G, H, n]; each output is `merge_states` of its members, in order."""
+    G = len(group_offsets) - 1
+    outO, outL = [], []
+    for j in range(G):
+        a, b = group_offsets[j], group_offsets[j + 1]
+        Oj, Lj = merge_states(list(O[a:b]), list(lse[a:b]))
+        outO.append(Oj)
+        outL.append(Lj)
+    return np.stack(outO), np.stack(outL)
+
+
 def importance(weights: np.ndarray, rows: np.ndarray, q_offsets: Sequence[int]) -> np.ndarray:
     """Partition importance w[i, p] = mean over rows r of block i and heads h of the merge
     weight e^{lse_p - lse} (DiTango pages, "Methodology §1, Error Modeling / Anchor Steps":

@@ -31,6 +31,10 @@ SIGNATURES = {
                                         c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p]),
     "dit_state_merge": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_void_p]),
+    "dit_state_merge_masked": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, P_i32, c_int, P_u8,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dit_state_compose": (c_int, [c_void_p, c_void_p, c_int, P_i32, c_int, c_int, c_int, c_int, c_int,
+                                  c_void_p, c_void_p, c_void_p]),
     "dit_importance": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, P_i32, c_int,
                                c_void_p, c_void_p]),
     "dit_local_change_finalize": (c_int, [c_void_p, c_size_t, c_int, c_int, c_int, c_int, P_i32, c_int,

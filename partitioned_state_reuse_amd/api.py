@@ -105,6 +105,23 @@ def state_merge(cache_o, cache_lse, out, lse, *, stream=None) -> None:
                                       _stream(stream)))
 
 
+def state_merge_masked(cache_o, cache_lse, q_offsets, plane_select, out, lse, *, extra_o=None, extra_lse=None,
+                       stream=None) -> None:
+    """Merge, per query block, only the selected cache planes (plus an optional extra state)."""
+    P, B, S_q, H, D = cache_o.shape
+    _check(_lib.lib().dit_state_merge_masked(_ptr(cache_o), _ptr(cache_lse), B, S_q, H, D, P, _i32(q_offsets),
+                                             len(q_offsets) - 1, _u8(plane_select), _ptr(extra_o), _ptr(extra_lse),
+                                             _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def state_compose(cache_o, cache_lse, group_offsets, out_o, out_lse, *, stream=None) -> None:
+    """Compose runs of adjacent cached partition states into coarser group states."""
+    P, B, S_q, H, D = cache_o.shape
+    _check(_lib.lib().dit_state_compose(_ptr(cache_o), _ptr(cache_lse), P, _i32(group_offsets),
+                                        len(group_offsets) - 1, B, S_q, H, D, _ptr(out_o), _ptr(out_lse),
+                                        _stream(stream)))
+
+
 def importance(cache_lse, lse, q_offsets, importance_out, *, stream=None) -> None:
     P, B, H, S_q = cache_lse.shape
     _check(_lib.lib().dit_importance(_ptr(cache_lse), _ptr(lse), B, S_q, H, P, _i32(q_offsets),
@@ -183,6 +200,55 @@ class SelectiveAttention:
         nb = workspace_bytes(B, S_q, H, D, self.n_qb, self.P)
         self.workspace = torch.empty(max(nb, 4) // 4, dtype=torch.float32, device=device)
         self.valid = np.zeros((self.n_qb, self.P), dtype=np.uint8)
+
+    def step_overlapped(self, q, k, v, recompute, *, side_stream, scale=0.0):
+        """One selective step with the reuse work moved off the critical path: the reused
+        states are pre-merged into a partial state on `side_stream` while the attention
+        kernel recomputes the others on the current stream (the two touch disjoint cache
+        slots); the current stream then merges the fresh states with the partial."""
+        recompute = np.asarray(recompute, dtype=np.uint8).reshape(self.n_qb, self.P)
+        if any(not self.valid[i, p] for i in range(self.n_qb) for p in range(self.P) if not recompute[i, p]):
+            raise DitError(-5, status_string(-5))
+        if not hasattr(self, "partial_o"):
+            self.partial_o = torch.empty_like(self.out)
+            self.partial_lse = torch.empty_like(self.lse)
+        main = torch.cuda.current_stream()
+        ready = torch.cuda.Event()
+        ready.record(main)
+        side_stream.wait_event(ready)
+        state_merge_masked(self.cache_o, self.cache_lse, self.q_offsets, 1 - recompute, self.partial_o,
+                           self.partial_lse, stream=side_stream)
+        partition_attention(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
+                            local_part=self.local_part, scale=scale, stream=main)
+        done = torch.cuda.Event()
+        done.record(side_stream)
+        main.wait_event(done)
+        state_merge_masked(self.cache_o, self.cache_lse, self.q_offsets, recompute, self.out, self.lse,
+                           extra_o=self.partial_o, extra_lse=self.partial_lse, stream=main)
+        self.valid |= recompute
+
+    def compose(self, group_offsets, stream=None) -> "SelectiveAttention":
+        """Dynamic group compose: a new SelectiveAttention whose partitions are the groups
+        (runs of adjacent partitions given by `group_offsets`) and whose cache holds the
+        composed states; validity of a group = every member valid.  This object's cache
+        is left unchanged (free it to reclaim the memory)."""
+        go = list(group_offsets)
+        kvo = [self.kv_offsets[g] for g in go]
+        local = [next(j for j in range(len(go) - 1) if go[j] <= lp < go[j + 1]) for lp in self.local_part]
+        out = SelectiveAttention.__new__(SelectiveAttention)
+        out.B, out.S_q, out.S_kv, out.H, out.D = self.B, self.S_q, self.S_kv, self.H, self.D
+        out.q_offsets, out.kv_offsets, out.local_part = list(self.q_offsets), kvo, local
+        out.n_qb, out.P = self.n_qb, len(go) - 1
+        dev = self.cache_o.device
+        out.cache_o = torch.empty((out.P, self.B, self.S_q, self.H, self.D), dtype=torch.bfloat16, device=dev)
+        out.cache_lse = torch.empty((out.P, self.B, self.H, self.S_q), dtype=torch.float32, device=dev)
+        state_compose(self.cache_o, self.cache_lse, go, out.cache_o, out.cache_lse, stream=stream)
+        out.out, out.lse = self.out, self.lse
+        out.importance = torch.empty((self.B, out.n_qb, out.P), dtype=torch.float32, device=dev)
+        out.delta = self.delta
+        out.workspace = self.workspace
+        out.valid = np.stack([self.valid[:, go[j]:go[j + 1]].all(axis=1) for j in range(out.P)], axis=1).astype(np.uint8)
+        return out
 
     def step(self, q, k, v, recompute, *, want_importance=False, want_delta=False, scale=0.0, stream=None):
         recompute = np.asarray(recompute, dtype=np.uint8).reshape(self.n_qb, self.P)

@@ -188,6 +188,61 @@ int dit_state_merge(const void *cache_o, const float *cache_lse, int B, int S_q,
   }
 }
 
+int dit_state_merge_masked(const void *cache_o, const float *cache_lse, int B, int S_q, int H, int D, int P,
+                           const int32_t *q_offsets, int n_qb, const uint8_t *plane_select, const void *extra_o,
+                           const float *extra_lse, void *out, float *lse, void *stream) {
+  try {
+    if (!cache_o || !cache_lse || !out || !lse || !plane_select) return DIT_ERR_NULL;
+    if ((extra_o == nullptr) != (extra_lse == nullptr)) return DIT_ERR_NULL;
+    int st = check_dims(B, S_q, 0, H, D);
+    if (st) return st;
+    if (P < 1 || P > DIT_MAX_PARTITIONS) return DIT_ERR_SHAPE;
+    if ((st = check_q_offsets(q_offsets, n_qb, S_q))) return st;
+    dit::MergeSelect sel;
+    memset(&sel, 0, sizeof(sel));
+    sel.n_qb = n_qb;
+    sel.has_extra = extra_o != nullptr;
+    for (int i = 0; i <= n_qb; ++i) sel.q_off[i] = q_offsets[i];
+    for (int i = 0; i < n_qb; ++i)
+      for (int p = 0; p < P; ++p) {
+        if (plane_select[i * P + p] > 1) return DIT_ERR_MASK;
+        if (plane_select[i * P + p]) sel.plane_mask[i] |= (uint64_t)1 << p;
+      }
+    if (dit::launch_state_merge_masked(D, P, cache_o, cache_lse, extra_o, extra_lse, sel, out, lse, B, S_q, H,
+                                       as_stream(stream)) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+int dit_state_compose(const void *cache_o, const float *cache_lse, int P_in, const int32_t *group_offsets, int G,
+                      int B, int S_q, int H, int D, void *out_o, float *out_lse, void *stream) {
+  try {
+    if (!cache_o || !cache_lse || !out_o || !out_lse || !group_offsets) return DIT_ERR_NULL;
+    int st = check_dims(B, S_q, 0, H, D);
+    if (st) return st;
+    if (P_in < 1 || P_in > DIT_MAX_PARTITIONS || G < 1 || G > P_in) return DIT_ERR_SHAPE;
+    if (group_offsets[0] != 0 || group_offsets[G] != P_in) return DIT_ERR_OFFSETS;
+    for (int g = 0; g < G; ++g)
+      if (group_offsets[g + 1] <= group_offsets[g]) return DIT_ERR_OFFSETS;
+    const int64_t plane_lse = (int64_t)B * H * S_q;
+    const int64_t plane_o = plane_lse * D;
+    const uint16_t *in_o = (const uint16_t *)cache_o;
+    uint16_t *o = (uint16_t *)out_o;
+    for (int g = 0; g < G; ++g) {
+      const int a = group_offsets[g];
+      if (dit::launch_state_merge(D, group_offsets[g + 1] - a, in_o + a * plane_o, cache_lse + a * plane_lse,
+                                  o + g * plane_o, out_lse + g * plane_lse, B, S_q, H, as_stream(stream)) != hipSuccess)
+        return DIT_ERR_HIP;
+    }
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
 int dit_importance(const float *cache_lse, const float *lse, int B, int S_q, int H, int P,
                    const int32_t *q_offsets, int n_qb, float *importance_out, void *stream) {
   try {

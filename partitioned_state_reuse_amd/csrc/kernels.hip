@@ -560,6 +560,102 @@ __global__ __launch_bounds__(256) void state_merge_kernel(
   if (c == 0) lse_out[li] = L;
 }
 
+// Masked merge: as state_merge_kernel, but row r of query block i combines only the planes
+// selected for block i, plus an optional extra state (a partial composition made earlier).
+// Used to pre-merge the reused states on a second stream while the attention kernel
+// recomputes the others, and to finish with the fresh states and that partial.
+template <int D, int PMAX>
+__global__ __launch_bounds__(256) void state_merge_masked_kernel(
+    const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, const u16 *__restrict__ extra_o,
+    const float *__restrict__ extra_lse, const MergeSelect sel, u16 *__restrict__ out,
+    float *__restrict__ lse_out, const int S_q, const int H, const int P, const int64_t total_rh,
+    const int64_t plane_o, const int64_t plane_lse) {
+  constexpr int TPR = D / 8;
+  constexpr int RPW = 256 / TPR;
+  const int64_t rh = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  if (rh >= total_rh) return;
+  const int c = threadIdx.x % TPR;
+  const int64_t br = rh / H;
+  const int h = (int)(rh - br * H);
+  const int64_t b = br / S_q;
+  const int r = (int)(br - b * S_q);
+  const int64_t li = (b * H + h) * S_q + r;
+  // block of row r: last i with q_off[i] <= r
+  int lo = 0, hi = sel.n_qb - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sel.q_off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const uint64_t pm = sel.plane_mask[lo];
+
+  float lv[PMAX + 1];
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) {
+    lv[p] = (p < P && ((pm >> p) & 1)) ? cache_lse[p * plane_lse + li] : -INFINITY;
+    M = fmaxf(M, lv[p]);
+  }
+  lv[PMAX] = sel.has_extra ? extra_lse[li] : -INFINITY;
+  M = fmaxf(M, lv[PMAX]);
+  const bool any = M > -INFINITY;
+  float sum = 0.f;
+#pragma unroll
+  for (int p = 0; p <= PMAX; ++p) sum += (lv[p] > -INFINITY) ? __expf(lv[p] - M) : 0.f;
+  const float L = any ? M + __logf(sum) : -INFINITY;
+
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  auto add = [&](const u16 *src, float lp) {
+    if (lp > -INFINITY) {
+      const float w = __expf(lp - L);
+      const u32x4 u = __builtin_nontemporal_load((const u32x4 *)src);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[2 * t] += w * bf16_bits_to_f32(u[t] & 0xffffu);
+        acc[2 * t + 1] += w * bf16_bits_to_f32(u[t] >> 16);
+      }
+    }
+  };
+  const u16 *src = cache_o + rh * D + 8 * c;
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p)
+    if (p < P) add(src + p * plane_o, lv[p]);
+  if (sel.has_extra) add(extra_o + rh * D + 8 * c, lv[PMAX]);
+  uint4 res;
+  res.x = pack_bf16x2(acc[0], acc[1]);
+  res.y = pack_bf16x2(acc[2], acc[3]);
+  res.z = pack_bf16x2(acc[4], acc[5]);
+  res.w = pack_bf16x2(acc[6], acc[7]);
+  __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
+  if (c == 0) lse_out[li] = L;
+}
+
+template <int D>
+hipError_t merge_masked_dispatch(int P, const void *cache_o, const float *cache_lse, const void *extra_o,
+                                 const float *extra_lse, const MergeSelect &sel, void *out, float *lse,
+                                 int B, int S_q, int H, hipStream_t stream) {
+  const int64_t total_rh = (int64_t)B * S_q * H;
+  if (total_rh == 0) return hipSuccess;
+  constexpr int RPW = 256 / (D / 8);
+  const int64_t nwg = (total_rh + RPW - 1) / RPW;
+  const int64_t plane_o = total_rh * D;
+  const int64_t plane_lse = total_rh;
+  dim3 grid((unsigned)nwg), block(256);
+  const u16 *co = (const u16 *)cache_o;
+  const u16 *eo = (const u16 *)extra_o;
+  u16 *oo = (u16 *)out;
+  if (P <= 8)
+    hipLaunchKernelGGL((state_merge_masked_kernel<D, 8>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+  else if (P <= 16)
+    hipLaunchKernelGGL((state_merge_masked_kernel<D, 16>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+  else if (P <= 32)
+    hipLaunchKernelGGL((state_merge_masked_kernel<D, 32>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+  else
+    hipLaunchKernelGGL((state_merge_masked_kernel<D, 64>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+  return hipGetLastError();
+}
+
 // Fixed-order tree reduction of one float per thread over a 256-thread workgroup.
 __device__ __forceinline__ float block_sum_256(float x, float *sh) {
   sh[threadIdx.x] = x;
@@ -666,6 +762,15 @@ hipError_t launch_state_merge(int D, int P, const void *cache_o, const float *ca
   (void)hipGetLastError();
   if (D == 128) return merge_dispatch<128>(P, cache_o, cache_lse, out, lse, B, S_q, H, stream);
   return merge_dispatch<64>(P, cache_o, cache_lse, out, lse, B, S_q, H, stream);
+}
+
+hipError_t launch_state_merge_masked(int D, int P, const void *cache_o, const float *cache_lse,
+                                     const void *extra_o, const float *extra_lse, const MergeSelect &sel,
+                                     void *out, float *lse, int B, int S_q, int H, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (D == 128)
+    return merge_masked_dispatch<128>(P, cache_o, cache_lse, extra_o, extra_lse, sel, out, lse, B, S_q, H, stream);
+  return merge_masked_dispatch<64>(P, cache_o, cache_lse, extra_o, extra_lse, sel, out, lse, B, S_q, H, stream);
 }
 
 hipError_t launch_importance(const float *cache_lse, const float *lse, int B, int S_q, int H, int P,

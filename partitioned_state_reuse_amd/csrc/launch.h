@@ -56,6 +56,19 @@ hipError_t launch_partition_attention(int D, const void *q, const void *k, const
                                       void *cache_o, float *cache_lse, float *delta_partials,
                                       const AttnDesc &desc, float scale_log2, hipStream_t stream);
 
+// Plane selection of a masked merge: row r of block i merges plane p when bit p of
+// plane_mask[i] is set, plus the extra state when there is one.
+struct MergeSelect {
+  int32_t n_qb;
+  int32_t has_extra;
+  int32_t q_off[DIT_MAX_BLOCKS + 1];
+  uint64_t plane_mask[DIT_MAX_BLOCKS];
+};
+
+hipError_t launch_state_merge_masked(int D, int P, const void *cache_o, const float *cache_lse,
+                                     const void *extra_o, const float *extra_lse, const MergeSelect &sel,
+                                     void *out, float *lse, int B, int S_q, int H, hipStream_t stream);
+
 hipError_t launch_state_merge(int D, int P, const void *cache_o, const float *cache_lse,
                               void *out, float *lse, int B, int S_q, int H, hipStream_t stream);
 

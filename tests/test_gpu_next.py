@@ -1,0 +1,115 @@
+"""GPU parity of the rows built beyond the core step: Dynamic Group Compose (composed
+cached states, and a step continued at group granularity on the composed cache)."""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads as W
+import _parity as PT
+from partitioned_state_reuse_amd import api
+
+pytestmark = pytest.mark.gpu
+
+
+def test_group_compose_then_continue_at_group_level():
+    w = W.workload("video720p", grid=(5, 18, 32), H=4)
+    rows = np.arange(w.S_q)
+    ones = np.ones((w.n_qb, w.P), np.uint8)
+    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
+    g = PT.GpuRun(w)
+    o = PT.OracleRun(w, rows)
+    g.step(Xp, ones)
+    o.step(Xp, ones)
+    go = w.group_offsets                              # pairs of adjacent partitions
+    sa2 = g.sa.compose(go)
+    torch.cuda.synchronize()
+    # composed planes against the oracle's composition of its stored states
+    cO, cL = oracle.compose_states(o.cache.stored_O, o.cache.stored_lse, go)
+    gO = PT.bf16_to_f64(sa2.cache_o[:, 0])
+    gL = sa2.cache_lse[:, 0].double().cpu().numpy()
+    assert np.abs(gO - cO).max() <= PT.O_ABS_TOL
+    assert np.linalg.norm(gO - cO) / np.linalg.norm(cO) <= PT.O_REL_FRO_TOL
+    assert np.abs(gL - cL).max() <= PT.LSE_ABS_TOL
+    # and against the state of the union computed directly (no recomputation needed)
+    ue = oracle.compose_states(o.cache.exact_O, o.cache.exact_lse, go)
+    assert np.abs(gO - ue[0]).max() <= PT.O_ABS_TOL
+    # one more step at group granularity: 4 of 8 groups recomputed by distance
+    G = len(go) - 1
+    local_g = [i // 2 for i in range(w.n_qb)]
+    assert sa2.local_part == local_g
+    rp = oracle.RefPlanner(w.n_qb, G, list(range(G + 1)), local_g, 0, 4, "distance")
+    mask_g, _ = rp.next(1)
+    g2 = PT.GpuRun.__new__(PT.GpuRun)
+    g2.w, g2.sa = w, sa2
+    g2.step(X, mask_g)
+    cache_g = oracle.StateCache(rows=rows, exact_O=ue[0], exact_lse=ue[1],
+                                stored_O=oracle.round_bf16(cO), stored_lse=oracle.round_f32(cL),
+                                valid=np.ones((w.n_qb, G), bool))
+    kvo = [w.kv_offsets[j] for j in go]
+    res = oracle.selective_step(W.to_f64(X.q[0]), W.to_f64(X.k[0]), W.to_f64(X.v[0]), rows, w.q_offsets,
+                                kvo, mask_g, cache_g, 1.0 / math.sqrt(w.D))
+    cmp = PT.compare_out(g2.out_rows(rows), g2.lse_rows(rows), res)
+    print("group-level step", cmp, flush=True)
+    assert cmp.ok(), str(cmp)
+
+
+def test_compose_rejects_bad_offsets():
+    sa = api.SelectiveAttention(1, 64, 64, 1, 64, [0, 64], [0, 16, 32, 48, 64], [0])
+    out_o = torch.empty((2, 1, 64, 1, 64), dtype=torch.bfloat16, device="cuda")
+    out_l = torch.empty((2, 1, 1, 64), dtype=torch.float32, device="cuda")
+    for bad in ([0, 2, 3], [0, 2, 2, 4], [1, 4]):
+        with pytest.raises(api.DitError):
+            api.state_compose(sa.cache_o, sa.cache_lse, bad, out_o, out_l)
+
+
+def test_overlapped_step_matches_oracle():
+    """Reused states pre-merged on a second stream during the attention kernel, then merged
+    with the fresh states: same result (to tolerance) as the oracle's selective step."""
+    w = W.workload("video720p", grid=(5, 18, 32), H=4)
+    rows = np.arange(w.S_q)
+    ones = np.ones((w.n_qb, w.P), np.uint8)
+    mask, _, _, _ = PT.masks_from_planners(w)
+    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
+    g = PT.GpuRun(w)
+    o = PT.OracleRun(w, rows)
+    g.step(Xp, ones)
+    o.step(Xp, ones)
+    side = torch.cuda.Stream()
+    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
+    g.sa.step_overlapped(q, k, v, mask, side_stream=side)
+    torch.cuda.synchronize()
+    res = o.step(X, mask)
+    cmp = PT.compare_out(g.out_rows(rows), g.lse_rows(rows), res)
+    print("overlapped step", cmp, flush=True)
+    assert cmp.ok(), str(cmp)
+    # the partial state alone is the merge of the reused planes
+    blk = oracle.block_of_rows(rows, w.q_offsets)
+    sel = [(1 - mask[blk, p]).astype(bool) for p in range(w.P)]
+    pO = PT.bf16_to_f64(g.sa.partial_o[0])
+    Os = [np.where(sel[p][:, None, None], o.cache.stored_O[p], 0.0) for p in range(w.P)]
+    Ls = [np.where(sel[p][None, :], o.cache.stored_lse[p], -np.inf) for p in range(w.P)]
+    rO, rL = oracle.merge_states(Os, Ls)
+    assert np.abs(pO - rO).max() <= PT.O_ABS_TOL
+
+
+def test_masked_merge_selects_planes_per_block():
+    """Selecting a single plane per block returns that plane's state (bf16 round trip)."""
+    S, H, D, P = 300, 2, 128, 4
+    qo = [0, 100, 300]
+    torch.manual_seed(3)
+    co = torch.randn((P, 1, S, H, D), device="cuda").to(torch.bfloat16)
+    cl = torch.randn((P, 1, H, S), device="cuda")
+    out = torch.empty((1, S, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, H, S), dtype=torch.float32, device="cuda")
+    sel = np.array([[0, 0, 1, 0], [1, 0, 0, 0]], np.uint8)
+    api.state_merge_masked(co, cl, qo, sel, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0, :100], co[2, 0, :100]) and torch.equal(out[0, 100:], co[0, 0, 100:])
+    assert torch.allclose(lse[0, :, :100], cl[2, 0, :, :100]) and torch.allclose(lse[0, :, 100:], cl[0, 0, :, 100:])
+    api.state_merge_masked(co, cl, qo, np.zeros_like(sel), out, lse)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()

@@ -399,3 +399,34 @@ def test_seeded_draws_are_chunk_consistent():
     full = W.normal_tokens(w.seed, W.T_Q, 0, 5000, 1, 4)
     part = W.normal_tokens(w.seed, W.T_Q, 1999, 4100, 1, 4)
     assert np.array_equal(full[1999:4100], part)
+
+
+# ----------------------------------------------------------------------------- group compose
+
+def test_compose_equals_attention_over_the_union():
+    """Composing the cached states of adjacent partitions gives, with no recomputation, the
+    state attention over the union of their keys has (brute force)."""
+    rng = np.random.default_rng(20)
+    q, k, v = rand_qkv(rng, 4, 30, 2, 4)
+    offs = [0, 3, 9, 9, 17, 24, 30]
+    Os, ls = states_of(q * 1.5, k, v, offs, 0.6)
+    groups = [0, 2, 4, 6]                      # partitions {0,1}, {2 (empty), 3}, {4,5}
+    cO, cL = oracle.compose_states(np.stack(Os), np.stack(ls), groups)
+    for j in range(3):
+        a, b = offs[groups[j]], offs[groups[j + 1]]
+        Ob, lb = brute_attention(q * 1.5, k[a:b], v[a:b], 0.6)
+        assert np.abs(cO[j] - Ob).max() < 1e-12 and np.abs(cL[j] - lb).max() < 1e-12
+
+
+def test_compose_is_associative_with_merge_and_recursive():
+    rng = np.random.default_rng(21)
+    O = rng.standard_normal((8, 5, 2, 3))
+    L = rng.standard_normal((8, 2, 5)) * 2
+    L[3] = -np.inf                              # an empty partition
+    full = OA.merge_states(list(O), list(L))
+    cO, cL = oracle.compose_states(O, L, [0, 2, 4, 6, 8])
+    m2 = OA.merge_states(list(cO), list(cL))
+    assert np.abs(m2[0] - full[0]).max() < 1e-12 and np.abs(m2[1] - full[1]).max() < 1e-12
+    ccO, ccL = oracle.compose_states(cO, cL, [0, 2, 4])
+    dO, dL = oracle.compose_states(O, L, [0, 4, 8])
+    assert np.abs(ccO - dO).max() < 1e-12 and np.abs(ccL - dL).max() < 1e-12
