@@ -311,6 +311,72 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] importance {imp_ms:.3f} ms, planner {planner_us:.1f} us/call, attention enqueue {enqueue_us:.1f} us")
 
+    # two-stream overlap: the reused states are pre-merged on a second stream during the
+    # attention kernel, then merged with the fresh states
+    side = torch.cuda.Stream()
+    for _ in range(args.warmup):
+        sa.step_overlapped(q, k, v, mask, side_stream=side, want_delta=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        m_t, _ = planner.next(t + 1)
+        sa.step_overlapped(q, k, v, m_t, side_stream=side, want_delta=True)
+    torch.cuda.synchronize()
+    ov_ms = (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
+    # dynamic group compose of the P cached states into the groups
+    go = w.group_offsets
+    G = len(go) - 1
+    comp_o = torch.empty((G, 1, w.S_q, w.H, w.D), dtype=torch.bfloat16, device=dev)
+    comp_l = torch.empty((G, 1, w.H, w.S_q), dtype=torch.float32, device=dev)
+    api.state_compose(sa.cache_o, sa.cache_lse, go, comp_o, comp_l, stream=stream)
+    c0_, c1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0_.record(stream)
+    for _ in range(5):
+        api.state_compose(sa.cache_o, sa.cache_lse, go, comp_o, comp_l, stream=stream)
+    c1_.record(stream)
+    torch.cuda.synchronize()
+    comp_ms = c0_.elapsed_time(c1_) / 5
+    comp_bytes = float(w.S_q * w.H * (w.P + G) * (2 * w.D + 4))
+    del comp_o, comp_l
+    log(f"[bench] overlapped step {ov_ms:.3f} ms (plain {ms_step:.3f}); group compose {comp_ms:.3f} ms "
+        f"({comp_bytes / (comp_ms * 1e-3) / 1e9:.0f} GB/s)")
+
+    # compressed (fp8 e4m3 + per-row-head scale) state cache: same step on its own cache
+    sa8 = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part,
+                                 cache_format="fp8")
+    sa8.step(q, k, v, np.ones((w.n_qb, w.P), np.uint8))
+    ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def fp8_step(t, e=None):
+        m_t, _ = planner.next(t)
+        if e:
+            e[0].record(stream)
+        api.partition_attention_fp8(q, k, v, w.q_offsets, w.kv_offsets, m_t, sa8.cache_o, sa8.cache_scale,
+                                    sa8.cache_lse, local_part=w.local_part, delta_partials=sa8.workspace,
+                                    stream=stream)
+        if e:
+            e[1].record(stream)
+        api.state_merge_fp8(sa8.cache_o, sa8.cache_scale, sa8.cache_lse, sa8.out, sa8.lse, stream=stream)
+        if e:
+            e[2].record(stream)
+        api.local_change_finalize(sa8.workspace, 1, w.S_q, w.H, w.D, w.q_offsets, sa8.delta, stream=stream)
+
+    for t in range(args.warmup):
+        fp8_step(t + 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        fp8_step(t + 1, ev8[t])
+    torch.cuda.synchronize()
+    fp8_ms = (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
+    fp8_attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev8]))
+    fp8_merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev8]))
+    # per row-head: P planes of D code bytes + scale + lse read, bf16 output + lse written
+    fp8_bytes = float(w.S_q * w.H * (w.P * (w.D + 8) + 2 * w.D + 4))
+    del sa8
+    log(f"[bench] fp8 cache step {fp8_ms:.3f} ms: attention {fp8_attn_ms:.3f} ms, merge {fp8_merge_ms:.3f} ms "
+        f"({fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9:.0f} GB/s)")
+
     # plain device copy of 4 GiB as the achievable-bandwidth reference (and PMC calibration)
     src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
     dst = torch.empty_like(src)
@@ -326,7 +392,7 @@ def main() -> int:
     log(f"[bench] device copy {copy_gbs:.0f} GB/s")
 
     traffic = measured_traffic(w.name)
-    attn_traffic = traffic.get("dit::partition_attention_kernel<128>")
+    attn_traffic = traffic.get("dit::partition_attention_kernel<128, false>")
     merge_traffic = traffic.get(f"dit::state_merge_kernel<128, {16 if w.P <= 16 else 32 if w.P <= 32 else 64}>")
     result = {
         "metric": "recomputed-attn TFLOP/s + merge GB/s at 75.6k tokens, % of MFMA/HBM peak",
@@ -348,13 +414,25 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic,
-                     "kernel": "partition_attention_kernel<128>", "ms": round(attn_ms, 4),
+                     "kernel": "partition_attention_kernel<128, false>", "ms": round(attn_ms, 4),
                      "algorithmic_flop": flop},
         "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4), "traffic": merge_traffic,
                            "kernel": "state_merge_kernel<128,16>", "ms": round(merge_ms, 4),
                            "algorithmic_bytes": mbytes, "device_copy_gbs": round(copy_gbs, 1)},
         "local_change_finalize_ms": round(fin_ms, 5),
+        "overlap_two_streams": {"ms_per_step": round(ov_ms, 4), "plain_ms_per_step": round(ms_step, 4),
+                                "value": round(flop / (ov_ms * 1e-3) / 1e12, 2)},
+        "group_compose": {"ms": round(comp_ms, 4), "gbs": round(comp_bytes / (comp_ms * 1e-3) / 1e9, 1),
+                          "frac": round(comp_bytes / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes": comp_bytes, "planes": f"{w.P} -> {len(w.group_offsets) - 1}"},
+        "fp8_cache": {"ms_per_step": round(fp8_ms, 4), "attention_ms": round(fp8_attn_ms, 4),
+                      "attention_tflops": round(flop / (fp8_attn_ms * 1e-3) / 1e12, 1),
+                      "merge_ms": round(fp8_merge_ms, 4),
+                      "merge_gbs": round(fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9, 1),
+                      "merge_frac": round(fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "merge_algorithmic_bytes": fp8_bytes,
+                      "value": round(flop / (fp8_ms * 1e-3) / 1e12, 2)},
         "importance_ms": round(imp_ms, 4),
         "importance_gbs": round(float(w.S_q * w.H * w.P * 8) / (imp_ms * 1e-3) / 1e9, 1),
         "planner_us_per_step": round(planner_us, 2),

@@ -150,6 +150,39 @@ int dit_state_merge(const void *cache_o, const float *cache_lse,
                     void *stream);
 
 /*
+ * Compressed state cache (the cache compression the pages name as future work: DiTango,
+ * technical summary, "Significance and Claims", limitations).  Same operation as
+ * dit_partition_attention and dit_state_merge, with each cached O_p slot held as OCP fp8
+ * e4m3 codes plus one f32 scale per (partition, batch, head, row):
+ *   cache_q8     [P, B, S_q, H, D] u8    code c of element x: the e4m3 value nearest
+ *                                        x / s (round to nearest, ties to even)
+ *   cache_scale  [P, B, H, S_q] f32      s = max_d |O_p| / 448 over the row-head's D values
+ *                                        (0 for an all-zero state: codes 0)
+ *   cache_lse    as for the bf16 cache
+ * The slot's value is s * e4m3(c); per element it is within max(2^-4 |x|, 2^-10 s) of the
+ * fp32 state.  Per row-head and plane the cache holds D + 8 bytes instead of 2 D + 4.
+ * delta_partials of dit_partition_attention_fp8 compare the dequantized new and old slot
+ * values.  dit_state_merge_fp8 folds each plane's scale into its merge weight,
+ * out = sum_p s_p e^{lse_p - lse} e4m3(c_p), accumulated in fp32, written as bf16.
+ * Argument checks and errors as for the bf16 calls; cache_scale must be non-NULL.
+ */
+int dit_partition_attention_fp8(const void *q, const void *k, const void *v,
+                                int B, int S_q, int S_kv, int H, int D,
+                                const int32_t *q_offsets, int n_qb,
+                                const int32_t *kv_offsets, int P,
+                                const int32_t *local_part,
+                                const uint8_t *recompute,
+                                void *cache_q8, float *cache_scale, float *cache_lse,
+                                float softmax_scale,
+                                void *delta_partials, size_t workspace_bytes,
+                                void *stream);
+
+int dit_state_merge_fp8(const void *cache_q8, const float *cache_scale, const float *cache_lse,
+                        int B, int S_q, int H, int D, int P,
+                        void *out, float *lse,
+                        void *stream);
+
+/*
  * Masked state merge: like dit_state_merge, but row r of query block i composes only the
  * cache planes p with plane_select[i * P + p] = 1 (host [n_qb * P], values 0/1), plus the
  * extra state (extra_o [B, S_q, H, D] bf16, extra_lse [B, H, S_q] f32) when both pointers

@@ -105,6 +105,52 @@ def round_f32(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
+FP8_MAX = 448.0   # largest finite OCP e4m3 value
+
+
+def round_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round to the OCP fp8 e4m3 grid (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+    normals 2^-6 .. 448, subnormals k * 2^-9), nearest with ties to even.  Values above
+    464 would round past 448 (the largest finite code) and are rejected.  Returned as
+    float64."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > 464.0):
+        raise ValueError("value beyond the e4m3 range")
+    a = np.abs(x)
+    # spacing of the grid at |x|: 2^(e-3) for normals (e = floor(log2 a) >= -6), 2^-9 below
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    ulp = np.exp2(e - 3.0)
+    q = a / ulp
+    r = np.floor(q)
+    frac = q - r
+    up = (frac > 0.5) | ((frac == 0.5) & (np.fmod(r, 2.0) == 1.0))
+    r = r + up
+    return np.sign(x) * r * ulp
+
+
+def decode_fp8_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP e4m3 codes (uint8) from the bit fields: sign (bit 7), exponent E (bits
+    6..3, bias 7), mantissa M (bits 2..0); E = 0 gives M * 2^-9, E = 15 with M = 7 is NaN,
+    otherwise (1 + M / 8) * 2^(E - 7).  Returned as float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    E = (c >> 3) & 15
+    M = (c & 7).astype(np.float64)
+    mag = np.where(E == 0, M * 2.0 ** -9, (1.0 + M / 8.0) * np.exp2(E - 7.0))
+    mag = np.where((E == 15) & (M == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_store(O: np.ndarray) -> np.ndarray:
+    """The compressed cache's view of states O [..., D]: per (row, head) scale
+    s = max_d |O| / 448 and e4m3 codes of O / s; returns the dequantized s * code."""
+    amax = np.abs(O).max(axis=-1, keepdims=True)
+    s = amax / FP8_MAX
+    safe = np.where(s > 0, s, 1.0)
+    return np.where(s > 0, round_fp8_e4m3(np.clip(O / safe, -FP8_MAX, FP8_MAX)) * safe, 0.0)
+
+
 # --------------------------------------------------------------------------------------
 # Selective step with a state cache
 # --------------------------------------------------------------------------------------

@@ -29,6 +29,11 @@ SIGNATURES = {
     "dit_partition_attention": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                         P_i32, c_int, P_i32, c_int, P_i32, P_u8,
                                         c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p]),
+    "dit_partition_attention_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                            P_i32, c_int, P_i32, c_int, P_i32, P_u8,
+                                            c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p]),
+    "dit_state_merge_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                    c_void_p, c_void_p, c_void_p]),
     "dit_state_merge": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_void_p]),
     "dit_state_merge_masked": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, P_i32, c_int, P_u8,

@@ -99,6 +99,25 @@ def partition_attention(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cach
         float(scale), _ptr(delta_partials), ws_bytes, _stream(stream)))
 
 
+def partition_attention_fp8(q, k, v, q_offsets, kv_offsets, recompute, cache_q8, cache_scale, cache_lse, *,
+                            local_part=None, scale: float = 0.0, delta_partials=None, stream=None) -> None:
+    """partition_attention into the compressed cache (cache_q8 uint8 e4m3 codes,
+    cache_scale one f32 scale per partition, batch, head and row)."""
+    B, S_q, S_kv, H, D = _dims(q, k)
+    n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
+    ws_bytes = 0 if delta_partials is None else delta_partials.numel() * delta_partials.element_size()
+    _check(_lib.lib().dit_partition_attention_fp8(
+        _ptr(q), _ptr(k), _ptr(v), B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
+        None if local_part is None else _i32(local_part), _u8(recompute), _ptr(cache_q8), _ptr(cache_scale),
+        _ptr(cache_lse), float(scale), _ptr(delta_partials), ws_bytes, _stream(stream)))
+
+
+def state_merge_fp8(cache_q8, cache_scale, cache_lse, out, lse, *, stream=None) -> None:
+    P, B, S_q, H, D = cache_q8.shape
+    _check(_lib.lib().dit_state_merge_fp8(_ptr(cache_q8), _ptr(cache_scale), _ptr(cache_lse), B, S_q, H, D, P,
+                                          _ptr(out), _ptr(lse), _stream(stream)))
+
+
 def state_merge(cache_o, cache_lse, out, lse, *, stream=None) -> None:
     P, B, S_q, H, D = cache_o.shape
     _check(_lib.lib().dit_state_merge(_ptr(cache_o), _ptr(cache_lse), B, S_q, H, D, P, _ptr(out), _ptr(lse),
@@ -186,12 +205,22 @@ class SelectiveAttention:
     its state has been computed) and the local-change workspace."""
 
     def __init__(self, B: int, S_q: int, S_kv: int, H: int, D: int, q_offsets: Sequence[int],
-                 kv_offsets: Sequence[int], local_part: Sequence[int], device="cuda"):
+                 kv_offsets: Sequence[int], local_part: Sequence[int], device="cuda", cache_format="bf16"):
+        """cache_format "bf16" keeps O_p in bfloat16; "fp8" keeps e4m3 codes plus one scale
+        per (partition, batch, head, row) (about half the bytes; step() only)."""
+        if cache_format not in ("bf16", "fp8"):
+            raise ValueError(f"cache_format must be 'bf16' or 'fp8', got {cache_format!r}")
         self.B, self.S_q, self.S_kv, self.H, self.D = B, S_q, S_kv, H, D
         self.q_offsets, self.kv_offsets = list(q_offsets), list(kv_offsets)
         self.local_part = list(local_part)
         self.n_qb, self.P = len(q_offsets) - 1, len(kv_offsets) - 1
-        self.cache_o = torch.empty((self.P, B, S_q, H, D), dtype=torch.bfloat16, device=device)
+        self.cache_format = cache_format
+        if cache_format == "fp8":
+            self.cache_o = torch.empty((self.P, B, S_q, H, D), dtype=torch.uint8, device=device)
+            self.cache_scale = torch.empty((self.P, B, H, S_q), dtype=torch.float32, device=device)
+        else:
+            self.cache_o = torch.empty((self.P, B, S_q, H, D), dtype=torch.bfloat16, device=device)
+            self.cache_scale = None
         self.cache_lse = torch.empty((self.P, B, H, S_q), dtype=torch.float32, device=device)
         self.out = torch.empty((B, S_q, H, D), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((B, H, S_q), dtype=torch.float32, device=device)
@@ -201,11 +230,12 @@ class SelectiveAttention:
         self.workspace = torch.empty(max(nb, 4) // 4, dtype=torch.float32, device=device)
         self.valid = np.zeros((self.n_qb, self.P), dtype=np.uint8)
 
-    def step_overlapped(self, q, k, v, recompute, *, side_stream, scale=0.0):
+    def step_overlapped(self, q, k, v, recompute, *, side_stream, want_delta=False, scale=0.0):
         """One selective step with the reuse work moved off the critical path: the reused
         states are pre-merged into a partial state on `side_stream` while the attention
         kernel recomputes the others on the current stream (the two touch disjoint cache
         slots); the current stream then merges the fresh states with the partial."""
+        self._bf16_only("step_overlapped")
         recompute = np.asarray(recompute, dtype=np.uint8).reshape(self.n_qb, self.P)
         if any(not self.valid[i, p] for i in range(self.n_qb) for p in range(self.P) if not recompute[i, p]):
             raise DitError(-5, status_string(-5))
@@ -218,20 +248,27 @@ class SelectiveAttention:
         side_stream.wait_event(ready)
         state_merge_masked(self.cache_o, self.cache_lse, self.q_offsets, 1 - recompute, self.partial_o,
                            self.partial_lse, stream=side_stream)
+        do_delta = want_delta and all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
         partition_attention(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
-                            local_part=self.local_part, scale=scale, stream=main)
+                            local_part=self.local_part, scale=scale,
+                            delta_partials=self.workspace if do_delta else None, stream=main)
         done = torch.cuda.Event()
         done.record(side_stream)
         main.wait_event(done)
         state_merge_masked(self.cache_o, self.cache_lse, self.q_offsets, recompute, self.out, self.lse,
                            extra_o=self.partial_o, extra_lse=self.partial_lse, stream=main)
+        if do_delta:
+            local_change_finalize(self.workspace, self.B, self.S_q, self.H, self.D, self.q_offsets, self.delta,
+                                  stream=main)
         self.valid |= recompute
+        return do_delta
 
     def compose(self, group_offsets, stream=None) -> "SelectiveAttention":
         """Dynamic group compose: a new SelectiveAttention whose partitions are the groups
         (runs of adjacent partitions given by `group_offsets`) and whose cache holds the
         composed states; validity of a group = every member valid.  This object's cache
         is left unchanged (free it to reclaim the memory)."""
+        self._bf16_only("compose")
         go = list(group_offsets)
         kvo = [self.kv_offsets[g] for g in go]
         local = [next(j for j in range(len(go) - 1) if go[j] <= lp < go[j + 1]) for lp in self.local_part]
@@ -239,6 +276,7 @@ class SelectiveAttention:
         out.B, out.S_q, out.S_kv, out.H, out.D = self.B, self.S_q, self.S_kv, self.H, self.D
         out.q_offsets, out.kv_offsets, out.local_part = list(self.q_offsets), kvo, local
         out.n_qb, out.P = self.n_qb, len(go) - 1
+        out.cache_format, out.cache_scale = "bf16", None
         dev = self.cache_o.device
         out.cache_o = torch.empty((out.P, self.B, self.S_q, self.H, self.D), dtype=torch.bfloat16, device=dev)
         out.cache_lse = torch.empty((out.P, self.B, self.H, self.S_q), dtype=torch.float32, device=dev)
@@ -250,10 +288,28 @@ class SelectiveAttention:
         out.valid = np.stack([self.valid[:, go[j]:go[j + 1]].all(axis=1) for j in range(out.P)], axis=1).astype(np.uint8)
         return out
 
+    def _bf16_only(self, what: str) -> None:
+        if self.cache_format != "bf16":
+            raise DitError(-7, f"{what} needs the bf16 state cache")
+
     def step(self, q, k, v, recompute, *, want_importance=False, want_delta=False, scale=0.0, stream=None):
         recompute = np.asarray(recompute, dtype=np.uint8).reshape(self.n_qb, self.P)
         local_valid = all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
         do_delta = want_delta and local_valid
+        if self.cache_format == "fp8":
+            if any(not self.valid[i, p] for i in range(self.n_qb) for p in range(self.P) if not recompute[i, p]):
+                raise DitError(-5, status_string(-5))
+            partition_attention_fp8(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o,
+                                    self.cache_scale, self.cache_lse, local_part=self.local_part, scale=scale,
+                                    delta_partials=self.workspace if do_delta else None, stream=stream)
+            state_merge_fp8(self.cache_o, self.cache_scale, self.cache_lse, self.out, self.lse, stream=stream)
+            if want_importance:
+                importance(self.cache_lse, self.lse, self.q_offsets, self.importance, stream=stream)
+            if do_delta:
+                local_change_finalize(self.workspace, self.B, self.S_q, self.H, self.D, self.q_offsets, self.delta,
+                                      stream=stream)
+            self.valid |= recompute
+            return do_delta
         attn_partitioned(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
                          self.out, self.lse, local_part=self.local_part, cache_valid=self.valid, scale=scale,
                          importance_out=self.importance if want_importance else None,

@@ -164,8 +164,45 @@ int dit_partition_attention(const void *q, const void *k, const void *v, int B, 
                         recompute, nullptr, cache_o, cache_lse, want_delta, delta_partials,
                         workspace_bytes, desc);
     if (st) return st;
-    if (dit::launch_partition_attention(D, q, k, v, cache_o, cache_lse, (float *)delta_partials, desc,
+    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse, (float *)delta_partials, desc,
                                         scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+int dit_partition_attention_fp8(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H, int D,
+                                const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P,
+                                const int32_t *local_part, const uint8_t *recompute, void *cache_q8,
+                                float *cache_scale, float *cache_lse, float softmax_scale, void *delta_partials,
+                                size_t workspace_bytes, void *stream) {
+  try {
+    if (!cache_scale) return DIT_ERR_NULL;
+    AttnDesc desc;
+    const bool want_delta = delta_partials != nullptr;
+    int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute, nullptr,
+                        cache_q8, cache_lse, want_delta, delta_partials, workspace_bytes, desc);
+    if (st) return st;
+    if (dit::launch_partition_attention(D, true, q, k, v, cache_q8, cache_scale, cache_lse, (float *)delta_partials,
+                                        desc, scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+int dit_state_merge_fp8(const void *cache_q8, const float *cache_scale, const float *cache_lse, int B, int S_q,
+                        int H, int D, int P, void *out, float *lse, void *stream) {
+  try {
+    if (!cache_q8 || !cache_scale || !cache_lse || !out || !lse) return DIT_ERR_NULL;
+    int st = check_dims(B, S_q, 0, H, D);
+    if (st) return st;
+    if (P < 1 || P > DIT_MAX_PARTITIONS) return DIT_ERR_SHAPE;
+    if (dit::launch_state_merge_fp8(D, P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, as_stream(stream)) !=
+        hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
   } catch (...) {
@@ -294,7 +331,7 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v, int B, int
                         cache_valid, cache_o, cache_lse, want_delta, workspace, workspace_bytes, desc);
     if (st) return st;
     hipStream_t s = as_stream(stream);
-    if (dit::launch_partition_attention(D, q, k, v, cache_o, cache_lse, want_delta ? (float *)workspace : nullptr,
+    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse, want_delta ? (float *)workspace : nullptr,
                                         desc, scale_log2_of(softmax_scale, D), s) != hipSuccess)
       return DIT_ERR_HIP;
     if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, s) != hipSuccess)

@@ -20,6 +20,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -127,11 +128,11 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ k, const u16 *__restrict__ v,
-    u16 *__restrict__ cache_o, float *__restrict__ cache_lse, float *__restrict__ delta_part,
-    const AttnDesc desc, const float scale_log2) {
+    void *__restrict__ cache_o, float *__restrict__ cache_scale, float *__restrict__ cache_lse,
+    float *__restrict__ delta_part, const AttnDesc desc, const float scale_log2) {
   using G = TileGeom<D>;
   constexpr int KK = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -445,8 +446,54 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   const float lse_nat = empty ? -INFINITY : (m + __log2f(ltot)) * kLn2;
   const bool is_local = delta_part != nullptr && desc.local_part[blk] == p;
   float dnum = 0.f, dden = 0.f;
-  if (qvalid) {
-    u16 *op = cache_o + ((((int64_t)p * desc.B + b) * desc.S_q + q0 + qrow) * H + head) * D;
+  const int64_t slot = ((int64_t)p * desc.B + b) * desc.S_q + q0 + qrow;           // [P, B, S_q]
+  const int64_t lslot = (((int64_t)p * desc.B + b) * H + head) * desc.S_q + q0 + qrow;  // [P, B, H, S_q]
+  if constexpr (FP8) {
+    // compressed slot: e4m3 codes of O / s with s = max_d |O| / 448 per (row, head); the
+    // lane pair holds the row's D values
+    float amax = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[db][r] * inv));
+    amax = pair_max(amax);
+    const float sc = amax / 448.f;
+    const float inv_s = amax > 0.f ? 448.f / amax : 0.f;
+    if (qvalid) {
+      uint8_t *op = (uint8_t *)cache_o + (slot * H + head) * D;
+      const float old_s = is_local ? cache_scale[lslot] : 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * hh;
+          float x[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) x[t] = (o[db][4 * g + t] * inv) * inv_s;
+          int wq = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+          wq = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wq, true);
+          if (is_local) {
+            const int od = *(const int *)(op + d0);
+            const f32x2 nv[2] = {__builtin_amdgcn_cvt_pk_f32_fp8(wq, false), __builtin_amdgcn_cvt_pk_f32_fp8(wq, true)};
+            const f32x2 ov[2] = {__builtin_amdgcn_cvt_pk_f32_fp8(od, false), __builtin_amdgcn_cvt_pk_f32_fp8(od, true)};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float n0 = nv[t >> 1][t & 1] * sc;
+              const float o0 = ov[t >> 1][t & 1] * old_s;
+              dnum += (n0 - o0) * (n0 - o0);
+              dden += o0 * o0;
+            }
+          }
+          *(int *)(op + d0) = wq;
+        }
+      }
+      if (hh == 0) {
+        cache_lse[lslot] = lse_nat;
+        cache_scale[lslot] = sc;
+      }
+    }
+  } else if (qvalid) {
+    u16 *op = (u16 *)cache_o + (slot * H + head) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -469,8 +516,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
         *(uint2 *)(op + d0) = nw;
       }
     }
-    if (hh == 0)
-      cache_lse[(((int64_t)p * desc.B + b) * H + head) * desc.S_q + q0 + qrow] = lse_nat;
+    if (hh == 0) cache_lse[lslot] = lse_nat;
   }
   if (is_local) {
 #pragma unroll
@@ -558,6 +604,91 @@ __global__ __launch_bounds__(256) void state_merge_kernel(
   res.w = pack_bf16x2(acc[6], acc[7]);
   __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
   if (c == 0) lse_out[li] = L;
+}
+
+// State merge over the compressed cache: per row-head, plane p holds e4m3 codes and a scale
+// s_p; the scale folds into the merge weight, w_p = s_p e^{lse_p - lse}.  One thread per 8
+// consecutive d (8-byte loads).
+template <int D, int PMAX>
+__global__ __launch_bounds__(256) void state_merge_fp8_kernel(
+    const uint8_t *__restrict__ cache_q8, const float *__restrict__ cache_scale,
+    const float *__restrict__ cache_lse, u16 *__restrict__ out, float *__restrict__ lse_out,
+    const int S_q, const int H, const int P, const int64_t total_rh, const int64_t plane_o,
+    const int64_t plane_lse) {
+  constexpr int TPR = D / 8;
+  constexpr int RPW = 256 / TPR;
+  const int64_t rh = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  if (rh >= total_rh) return;
+  const int c = threadIdx.x % TPR;
+  const int64_t br = rh / H;
+  const int h = (int)(rh - br * H);
+  const int64_t b = br / S_q;
+  const int64_t r = br - b * S_q;
+  const int64_t li = (b * H + h) * S_q + r;
+
+  float lv[PMAX];
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) {
+    lv[p] = (p < P) ? cache_lse[p * plane_lse + li] : -INFINITY;
+    M = fmaxf(M, lv[p]);
+  }
+  const bool any = M > -INFINITY;
+  float sum = 0.f;
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) sum += (lv[p] > -INFINITY) ? __expf(lv[p] - M) : 0.f;
+  const float L = any ? M + __logf(sum) : -INFINITY;
+
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const uint8_t *src = cache_q8 + rh * D + 8 * c;
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) {
+    if (p < P) {
+      const float w = (lv[p] > -INFINITY) ? __expf(lv[p] - L) * cache_scale[p * plane_lse + li] : 0.f;
+      const u32x2 u = __builtin_nontemporal_load((const u32x2 *)(src + p * plane_o));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], true);
+        acc[4 * t + 0] += w * lo[0];
+        acc[4 * t + 1] += w * lo[1];
+        acc[4 * t + 2] += w * hi[0];
+        acc[4 * t + 3] += w * hi[1];
+      }
+    }
+  }
+  uint4 res;
+  res.x = pack_bf16x2(acc[0], acc[1]);
+  res.y = pack_bf16x2(acc[2], acc[3]);
+  res.z = pack_bf16x2(acc[4], acc[5]);
+  res.w = pack_bf16x2(acc[6], acc[7]);
+  __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
+  if (c == 0) lse_out[li] = L;
+}
+
+template <int D>
+hipError_t merge_fp8_dispatch(int P, const void *cache_q8, const float *cache_scale, const float *cache_lse,
+                              void *out, float *lse, int B, int S_q, int H, hipStream_t stream) {
+  const int64_t total_rh = (int64_t)B * S_q * H;
+  if (total_rh == 0) return hipSuccess;
+  constexpr int RPW = 256 / (D / 8);
+  const int64_t nwg = (total_rh + RPW - 1) / RPW;
+  const int64_t plane_o = total_rh * D;
+  const int64_t plane_lse = total_rh;
+  dim3 grid((unsigned)nwg), block(256);
+  const uint8_t *cq = (const uint8_t *)cache_q8;
+  u16 *oo = (u16 *)out;
+  if (P <= 8)
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 8>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+  else if (P <= 16)
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 16>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+  else if (P <= 32)
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 32>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+  else
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 64>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+  return hipGetLastError();
 }
 
 // Masked merge: as state_merge_kernel, but row r of query block i combines only the planes
@@ -739,22 +870,35 @@ hipError_t merge_dispatch(int P, const void *cache_o, const float *cache_lse, vo
 
 }  // namespace
 
-hipError_t launch_partition_attention(int D, const void *q, const void *k, const void *v,
-                                      void *cache_o, float *cache_lse, float *delta_partials,
+hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, const void *k, const void *v,
+                                      void *cache_o, float *cache_scale, float *cache_lse, float *delta_partials,
                                       const AttnDesc &desc, float scale_log2, hipStream_t stream) {
   const int64_t nwg = (int64_t)desc.B * desc.H * desc.items_per_head;
   if (nwg == 0) return hipSuccess;
   (void)hipGetLastError();
   dim3 grid((unsigned)nwg), block(kWaves * 64);
-  if (D == 128)
-    hipLaunchKernelGGL(partition_attention_kernel<128>, grid, block, 0, stream, (const u16 *)q,
-                       (const u16 *)k, (const u16 *)v, (u16 *)cache_o, cache_lse, delta_partials, desc,
-                       scale_log2);
+  const u16 *qq = (const u16 *)q, *kk = (const u16 *)k, *vv = (const u16 *)v;
+  if (D == 128 && !fp8_cache)
+    hipLaunchKernelGGL((partition_attention_kernel<128, false>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
+                       cache_lse, delta_partials, desc, scale_log2);
+  else if (D == 128)
+    hipLaunchKernelGGL((partition_attention_kernel<128, true>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
+                       cache_lse, delta_partials, desc, scale_log2);
+  else if (!fp8_cache)
+    hipLaunchKernelGGL((partition_attention_kernel<64, false>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
+                       cache_lse, delta_partials, desc, scale_log2);
   else
-    hipLaunchKernelGGL(partition_attention_kernel<64>, grid, block, 0, stream, (const u16 *)q,
-                       (const u16 *)k, (const u16 *)v, (u16 *)cache_o, cache_lse, delta_partials, desc,
-                       scale_log2);
+    hipLaunchKernelGGL((partition_attention_kernel<64, true>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
+                       cache_lse, delta_partials, desc, scale_log2);
   return hipGetLastError();
+}
+
+hipError_t launch_state_merge_fp8(int D, int P, const void *cache_q8, const float *cache_scale,
+                                  const float *cache_lse, void *out, float *lse, int B, int S_q, int H,
+                                  hipStream_t stream) {
+  (void)hipGetLastError();
+  if (D == 128) return merge_fp8_dispatch<128>(P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, stream);
+  return merge_fp8_dispatch<64>(P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, stream);
 }
 
 hipError_t launch_state_merge(int D, int P, const void *cache_o, const float *cache_lse, void *out,

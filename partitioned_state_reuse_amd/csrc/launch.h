@@ -52,9 +52,15 @@ struct BlockDesc {
   int32_t tile_prefix[DIT_MAX_BLOCKS + 1];
 };
 
-hipError_t launch_partition_attention(int D, const void *q, const void *k, const void *v,
-                                      void *cache_o, float *cache_lse, float *delta_partials,
+// fp8_cache: cache_o holds e4m3 codes (1 byte per element) and cache_scale one scale per
+// (partition, batch, head, row); otherwise cache_o is bf16 and cache_scale is unused.
+hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, const void *k, const void *v,
+                                      void *cache_o, float *cache_scale, float *cache_lse, float *delta_partials,
                                       const AttnDesc &desc, float scale_log2, hipStream_t stream);
+
+hipError_t launch_state_merge_fp8(int D, int P, const void *cache_q8, const float *cache_scale,
+                                  const float *cache_lse, void *out, float *lse, int B, int S_q, int H,
+                                  hipStream_t stream);
 
 // Plane selection of a masked merge: row r of block i merges plane p when bit p of
 // plane_mask[i] is set, plus the extra state when there is one.

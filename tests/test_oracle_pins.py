@@ -430,3 +430,51 @@ def test_compose_is_associative_with_merge_and_recursive():
     ccO, ccL = oracle.compose_states(cO, cL, [0, 2, 4])
     dO, dL = oracle.compose_states(O, L, [0, 4, 8])
     assert np.abs(ccO - dO).max() < 1e-12 and np.abs(ccL - dL).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------- fp8 cache
+
+def test_fp8_e4m3_rounding_known_values():
+    """Values fixed by the OCP e4m3 format: bias 7, 3 mantissa bits, subnormal step 2^-9,
+    largest finite 448; round to nearest, ties to even."""
+    cases = {1.0: 1.0, 1.0625: 1.0, 1.09375: 1.125, 17.0: 16.0, 19.0: 20.0, 448.0: 448.0, 464.0: 448.0,
+             2.0 ** -9: 2.0 ** -9, 2.0 ** -10: 0.0, 1.5 * 2.0 ** -9: 2.0 ** -8, 0.1: 0.1015625,
+             -3.25: -3.25, 272.0: 256.0, 288.0: 288.0, 0.0: 0.0, 2.0 ** -6: 2.0 ** -6,
+             2.0 ** -6 - 2.0 ** -10: 2.0 ** -6}
+    for x, want in cases.items():
+        assert oracle.round_fp8_e4m3(np.array([x]))[0] == want, x
+    with pytest.raises(ValueError):
+        oracle.round_fp8_e4m3(np.array([465.0]))
+
+
+def test_fp8_store_error_bound():
+    rng = np.random.default_rng(22)
+    O = rng.standard_normal((50, 3, 64)) * np.exp(rng.uniform(-8, 4, (50, 3, 1)))
+    Q = oracle.fp8_store(O)
+    amax = np.abs(O).max(axis=-1, keepdims=True)
+    # every element within half a grid step of its scaled value: <= 2^-4 relative for
+    # values in the normal range of the scaled grid, <= 2^-10 * s absolute below it
+    s = amax / 448
+    err = np.abs(Q - O)
+    bound = np.maximum(np.abs(O) * 2.0 ** -4, s * 2.0 ** -10)
+    assert (err <= bound * (1 + 1e-12)).all()
+    assert np.array_equal(oracle.fp8_store(np.zeros((2, 1, 8))), np.zeros((2, 1, 8)))
+
+
+def test_fp8_decode_known_codes_and_grid():
+    """Codes fixed by the OCP e4m3 bit layout, and agreement of the bit-field decoder with
+    the rounding function: finite codes are fixed points of the rounding, rounded values
+    are values of codes, positive codes are strictly increasing."""
+    known = {0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x08: 2.0 ** -6, 0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0xFE: -448.0}
+    for c, want in known.items():
+        assert oracle.decode_fp8_e4m3(np.array([c], np.uint8))[0] == want, hex(c)
+    assert np.isnan(oracle.decode_fp8_e4m3(np.array([0x7F, 0xFF], np.uint8))).all()
+    vals = oracle.decode_fp8_e4m3(np.arange(256, dtype=np.uint8))
+    fin = np.isfinite(vals)
+    assert fin.sum() == 254
+    assert np.array_equal(oracle.round_fp8_e4m3(vals[fin]), vals[fin])
+    assert (np.diff(vals[:127]) > 0).all()
+    grid = set(vals[fin].tolist())
+    x = np.random.default_rng(23).uniform(-464, 464, 20000) * np.exp2(np.random.default_rng(24).integers(-14, 1, 20000))
+    assert set(oracle.round_fp8_e4m3(x).tolist()) <= grid
