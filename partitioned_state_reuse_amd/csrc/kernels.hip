@@ -138,12 +138,14 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   constexpr int DB = D / 32;        // 32-row blocks of O^T
   constexpr int MB = kBlockN / 32;  // 32-key blocks of S^T per tile
   constexpr int NC = kBlockN / 16;  // 16-key steps of O^T += V^T P^T per tile
-  // K and V tiles, two of each; separate variables so that the compiler knows a DMA into
-  // one buffer does not alias reads of another (no wait is inserted for it)
+  // Ring of kStages K and V tile buffers; separate variables so that the compiler knows a
+  // DMA into one buffer does not alias reads of another (no wait is inserted for it).
   __shared__ __attribute__((aligned(1024))) u16 k_lds0[G::TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) u16 k_lds1[G::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) u16 k_lds2[kStages > 2 ? G::TILE_ELEMS : 1];
   __shared__ __attribute__((aligned(1024))) u16 v_lds0[G::TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) u16 v_lds1[G::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) u16 v_lds2[kStages > 2 ? G::TILE_ELEMS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -194,12 +196,19 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   uint32_t koff_full[G::KB_PER_WAVE], voff_full[G::KB_PER_WAVE];
   dma_offsets<D, false>(rowstride, kBlockN, wave_u, lane, koff_full);
   dma_offsets<D, true>(rowstride, kBlockN, wave_u, lane, voff_full);
-  // Buffer parity is a compile-time argument everywhere: k_lds<t & 1> holds K tile t and
-  // v_lds<t & 1> holds V tile t.
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  auto kbuf = [&](auto par) -> u16 * { if constexpr (decltype(par)::value) return k_lds1; else return k_lds0; };
-  auto vbuf = [&](auto par) -> u16 * { if constexpr (decltype(par)::value) return v_lds1; else return v_lds0; };
+  // The ring stage is a compile-time argument everywhere: k_lds<t % kStages> holds K tile t
+  // and v_lds<t % kStages> holds V tile t.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  auto kbuf = [&](auto st) -> u16 * {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return k_lds0; else if constexpr (S == 1) return k_lds1; else return k_lds2;
+  };
+  auto vbuf = [&](auto st) -> u16 * {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return v_lds0; else if constexpr (S == 1) return v_lds1; else return v_lds2;
+  };
   auto issue_k = [&](int t, auto par) {
     if (t == ntiles - 1 && last_valid < kBlockN) {
       uint32_t off[G::KB_PER_WAVE];
@@ -218,10 +227,14 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       issue_tile<D>(vbase + t * tile_step, voff_full, vbuf(par), wave_u);
     }
   };
+  // prologue: the first kStages - 1 tiles in flight
   if (ntiles > 0) {
-    issue_k(0, P0{});
-    issue_v(0, P0{});
-    if (kPipeline && ntiles > 1) issue_k(1, P1{});
+    issue_k(0, S0{});
+    issue_v(0, S0{});
+  }
+  if (kStages > 2 && ntiles > 1) {
+    issue_k(1, S1{});
+    issue_v(1, S1{});
   }
 
   // ---- this lane's query row, as the B operand: Q[row][16 kk + 8 hh + 0..7]
@@ -351,91 +364,67 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       }
     }
   };
-  auto wait_tiles = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
-    __syncthreads();                     // ... and every wave's, and all reads of the old buffers are done
+  // Wait until this wave's copy of the oldest tile still in flight has landed (the loads of
+  // one tile per wave: vmcnt counts them in issue order), optionally leaving the next
+  // tile's loads in flight, then meet the other waves: afterwards the tile is complete in
+  // LDS and every wave is done reading the buffer that the next issue overwrites.
+  constexpr int kLoadsPerTile = 2 * G::KB_PER_WAVE;
+  static_assert(kStages == 2 || G::KB_PER_TILE % kWaves == 0, "every wave must issue the same loads per tile");
+  static_assert(kLoadsPerTile < 16, "vmcnt immediate");
+  auto wait_tiles = [&](bool next_in_flight) {
+    if (kStages > 2 && next_in_flight)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerTile);  // vmcnt(kLoadsPerTile)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+    // A bare barrier: __syncthreads() (or any release fence covering LDS) would also wait
+    // for the tile copy that is meant to stay in flight, since copies into LDS count as LDS
+    // writes.  The wait above covers the tile about to be read; this wave's reads of the
+    // buffer to be overwritten have completed (their data fed the MFMAs); the memory clobber
+    // keeps the compiler from moving LDS accesses across the barrier.
+    asm volatile("s_barrier" ::: "memory");
   };
 
-  if constexpr (kPipeline) {
-    // K runs one tile ahead of V.  Step kt (parity PAR of tile kt): tile kt+1's K Q^T MFMAs
-    // overlap tile kt's exponentials, and tile kt's V^T P^T MFMAs overlap tile kt+1's
-    // maximum.  On entry `cur` holds tile kt's scores and `mt_cur` their maximum; on exit
-    // they hold tile kt+1's.
-    auto step = [&](int kt, auto par, f32x16 (&cur)[MB], float &mt_cur) {
-      constexpr int PAR = decltype(par)::value;
-      using Pn = std::integral_constant<int, PAR ^ 1>;
-      if (kt + 2 < ntiles) issue_k(kt + 2, par);
-      issue_v(kt + 1, Pn{});
-      if (active) {
-        rescale(mt_cur);
-        bf16x8 pb[NC];
-        f32x16 nxt[MB];
-        qk(kbuf(Pn{}), nxt);
-        probs(cur, pb);
-        if (kt + 1 == ntiles - 1 && last_valid < kBlockN) mask_tail(nxt, last_valid);
-        pv(vbuf(par), pb);
-        mt_cur = tile_max(nxt);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) cur[mb] = nxt[mb];
-      }
-      wait_tiles();
-    };
-    auto last_step = [&](auto par, const f32x16 (&cur)[MB], float mt_cur) {
-      if (!active) return;
-      rescale(mt_cur);
-      bf16x8 pb[NC];
-      probs(cur, pb);
-      pv(vbuf(par), pb);
-    };
-    if (ntiles > 0) {
-      wait_tiles();
-      f32x16 cur[MB];
-      float mt_cur = 0.f;
-      if (active) {
-        qk(k_lds0, cur);
-        if (ntiles == 1 && last_valid < kBlockN) mask_tail(cur, last_valid);
-        mt_cur = tile_max(cur);
-      }
-      int kt = 0;
-      for (; kt + 2 < ntiles; kt += 2) {
-        step(kt, P0{}, cur, mt_cur);
-        step(kt + 1, P1{}, cur, mt_cur);
-      }
-      if (kt + 1 < ntiles) {
-        step(kt, P0{}, cur, mt_cur);
-        last_step(P1{}, cur, mt_cur);
-      } else {
-        last_step(P0{}, cur, mt_cur);
-      }
+  // Tile kt + kStages - 1 is copied while tile kt is consumed.
+  auto step = [&](int kt, auto st) {
+    constexpr int S = decltype(st)::value;
+    using Sa = std::integral_constant<int, (S + kStages - 1) % kStages>;
+    const bool ahead = kt + kStages - 1 < ntiles;
+    if (ahead) {
+      issue_k(kt + kStages - 1, Sa{});
+      issue_v(kt + kStages - 1, Sa{});
     }
-  } else {
-    // K and V of tile kt+1 are copied while tile kt is consumed.
-    auto step = [&](int kt, auto par) {
-      constexpr int PAR = decltype(par)::value;
-      using Pn = std::integral_constant<int, PAR ^ 1>;
-      if (kt + 1 < ntiles) {
-        issue_k(kt + 1, Pn{});
-        issue_v(kt + 1, Pn{});
+    if (active) {
+      f32x16 s[MB];
+      if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);
+      qk(kbuf(st), s);
+      if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(0);
+      if (kt == ntiles - 1 && last_valid < kBlockN) mask_tail(s, last_valid);
+      rescale(tile_max(s));
+      bf16x8 pb[NC];
+      probs(s, pb);
+      if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);
+      pv(vbuf(st), pb);
+      if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(0);
+    }
+    wait_tiles(ahead);
+  };
+  if (ntiles > 0) {
+    wait_tiles(kStages > 2 && ntiles > 1);
+    int kt = 0;
+    if constexpr (kStages > 2) {
+      for (; kt + 2 < ntiles; kt += 3) {
+        step(kt, S0{});
+        step(kt + 1, S1{});
+        step(kt + 2, S2{});
       }
-      if (active) {
-        f32x16 s[MB];
-        qk(kbuf(par), s);
-        if (kt == ntiles - 1 && last_valid < kBlockN) mask_tail(s, last_valid);
-        rescale(tile_max(s));
-        bf16x8 pb[NC];
-        probs(s, pb);
-        pv(vbuf(par), pb);
-      }
-      wait_tiles();
-    };
-    if (ntiles > 0) {
-      wait_tiles();
-      int kt = 0;
+      if (kt < ntiles) step(kt, S0{});
+      if (kt + 1 < ntiles) step(kt + 1, S1{});
+    } else {
       for (; kt + 1 < ntiles; kt += 2) {
-        step(kt, P0{});
-        step(kt + 1, P1{});
+        step(kt, S0{});
+        step(kt + 1, S1{});
       }
-      if (kt < ntiles) step(kt, P0{});
+      if (kt < ntiles) step(kt, S0{});
     }
   }
 
@@ -607,16 +596,18 @@ __global__ __launch_bounds__(256) void state_merge_kernel(
 }
 
 // State merge over the compressed cache: per row-head, plane p holds e4m3 codes and a scale
-// s_p; the scale folds into the merge weight, w_p = s_p e^{lse_p - lse}.  One thread per 8
-// consecutive d (8-byte loads).
+// s_p; the scale folds into the merge weight, w_p = s_p e^{lse_p - lse}.  One thread per
+// kFp8Dpt consecutive d (kFp8Dpt-byte code loads, non-temporal; bf16 output stores).
+constexpr int kFp8Dpt = DIT_MERGE_FP8_DPT;
 template <int D, int PMAX>
 __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
     const uint8_t *__restrict__ cache_q8, const float *__restrict__ cache_scale,
     const float *__restrict__ cache_lse, u16 *__restrict__ out, float *__restrict__ lse_out,
     const int S_q, const int H, const int P, const int64_t total_rh, const int64_t plane_o,
     const int64_t plane_lse) {
-  constexpr int TPR = D / 8;
+  constexpr int TPR = D / kFp8Dpt;
   constexpr int RPW = 256 / TPR;
+  constexpr int NW = kFp8Dpt / 4;  // 32-bit code words per thread and plane
   const int64_t rh = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
   if (rh >= total_rh) return;
   const int c = threadIdx.x % TPR;
@@ -639,17 +630,31 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
   for (int p = 0; p < PMAX; ++p) sum += (lv[p] > -INFINITY) ? __expf(lv[p] - M) : 0.f;
   const float L = any ? M + __logf(sum) : -INFINITY;
 
-  float acc[8];
+  float acc[kFp8Dpt];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  const uint8_t *src = cache_q8 + rh * D + 8 * c;
+  for (int e = 0; e < kFp8Dpt; ++e) acc[e] = 0.f;
+  const uint8_t *src = cache_q8 + rh * D + kFp8Dpt * c;
 #pragma unroll
   for (int p = 0; p < PMAX; ++p) {
     if (p < P) {
       const float w = (lv[p] > -INFINITY) ? __expf(lv[p] - L) * cache_scale[p * plane_lse + li] : 0.f;
-      const u32x2 u = __builtin_nontemporal_load((const u32x2 *)(src + p * plane_o));
+      uint32_t u[NW];
+      if constexpr (NW >= 4) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+        for (int q = 0; q < NW / 4; ++q) {
+          const u32x4 v4 = __builtin_nontemporal_load((const u32x4 *)(src + p * plane_o) + q);
+          u[4 * q + 0] = v4[0];
+          u[4 * q + 1] = v4[1];
+          u[4 * q + 2] = v4[2];
+          u[4 * q + 3] = v4[3];
+        }
+      } else {
+        const u32x2 v2 = __builtin_nontemporal_load((const u32x2 *)(src + p * plane_o));
+        u[0] = v2[0];
+        u[1] = v2[1];
+      }
+#pragma unroll
+      for (int t = 0; t < NW; ++t) {
         const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], false);
         const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], true);
         acc[4 * t + 0] += w * lo[0];
@@ -659,12 +664,11 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
       }
     }
   }
-  uint4 res;
-  res.x = pack_bf16x2(acc[0], acc[1]);
-  res.y = pack_bf16x2(acc[2], acc[3]);
-  res.z = pack_bf16x2(acc[4], acc[5]);
-  res.w = pack_bf16x2(acc[6], acc[7]);
-  __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
+#pragma unroll
+  for (int q = 0; q < kFp8Dpt / 8; ++q)
+    __builtin_nontemporal_store(u32x4{pack_bf16x2(acc[8 * q + 0], acc[8 * q + 1]), pack_bf16x2(acc[8 * q + 2], acc[8 * q + 3]),
+                                      pack_bf16x2(acc[8 * q + 4], acc[8 * q + 5]), pack_bf16x2(acc[8 * q + 6], acc[8 * q + 7])},
+                                (u32x4 *)(out + rh * D + kFp8Dpt * c + 8 * q));
   if (c == 0) lse_out[li] = L;
 }
 
@@ -673,7 +677,7 @@ hipError_t merge_fp8_dispatch(int P, const void *cache_q8, const float *cache_sc
                               void *out, float *lse, int B, int S_q, int H, hipStream_t stream) {
   const int64_t total_rh = (int64_t)B * S_q * H;
   if (total_rh == 0) return hipSuccess;
-  constexpr int RPW = 256 / (D / 8);
+  constexpr int RPW = 256 / (D / kFp8Dpt);
   const int64_t nwg = (total_rh + RPW - 1) / RPW;
   const int64_t plane_o = total_rh * D;
   const int64_t plane_lse = total_rh;

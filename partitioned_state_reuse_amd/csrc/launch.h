@@ -15,8 +15,8 @@ namespace dit {
 #ifndef DIT_ATTN_BLOCK_N
 #define DIT_ATTN_BLOCK_N 32
 #endif
-#ifndef DIT_ATTN_PIPELINE
-#define DIT_ATTN_PIPELINE 0
+#ifndef DIT_ATTN_STAGES
+#define DIT_ATTN_STAGES 2
 #endif
 #ifndef DIT_ATTN_MIN_BLOCKS
 #define DIT_ATTN_MIN_BLOCKS 3
@@ -24,7 +24,15 @@ namespace dit {
 constexpr int kWaves = DIT_ATTN_WAVES;      // waves per attention workgroup
 constexpr int kBlockM = 32 * kWaves;        // query rows per attention workgroup (32 per wave)
 constexpr int kBlockN = DIT_ATTN_BLOCK_N;   // keys per staged KV tile (32 or 64)
-constexpr bool kPipeline = DIT_ATTN_PIPELINE != 0;  // overlap tile j+1's K Q^T with tile j's softmax
+constexpr int kStages = DIT_ATTN_STAGES;    // K/V tile buffers in the LDS ring (2 or 3)
+#ifndef DIT_ATTN_SETPRIO
+#define DIT_ATTN_SETPRIO 0
+#endif
+// raise the wave priority while it issues MFMAs (K Q^T and V^T P^T), lower it for the softmax
+constexpr bool kSetPrio = DIT_ATTN_SETPRIO != 0;
+#ifndef DIT_MERGE_FP8_DPT
+#define DIT_MERGE_FP8_DPT 16
+#endif
 constexpr int kMinBlocks = DIT_ATTN_MIN_BLOCKS;     // attention workgroups resident per CU (register budget)
 
 // Work description of one partition-attention launch, passed by value as a kernel
