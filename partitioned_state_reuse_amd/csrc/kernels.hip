@@ -435,11 +435,26 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   const float lse_nat = empty ? -INFINITY : (m + __log2f(ltot)) * kLn2;
   const bool is_local = delta_part != nullptr && desc.local_part[blk] == p;
   float dnum = 0.f, dden = 0.f;
-  const int64_t slot = ((int64_t)p * desc.B + b) * desc.S_q + q0 + qrow;           // [P, B, S_q]
-  const int64_t lslot = (((int64_t)p * desc.B + b) * H + head) * desc.S_q + q0 + qrow;  // [P, B, H, S_q]
+  // The wave's rows go out through a staging buffer in LDS: one of the tile buffers, free
+  // now (every wave has passed the last tile's barrier and no copy is in flight).  The
+  // wave writes its rows there in the MFMA layout (lane (l32, hh) holds d = 32 db + 8 g +
+  // 4 hh + 0..3 of row l32), then reads them back row by row so that each row of the slot
+  // is written with contiguous 16-byte stores; the local-change sums read the old slot
+  // contents the same way.  16-byte chunk c of staged row r sits at chunk c ^ (r % chunks
+  // per row), so that the column-wise writes and the row-wise reads are free of bank
+  // conflicts.
+  static_assert(kWaves <= 4, "one staging buffer per wave");
+  char *stg = (char *)(wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1);
+  auto slot_of = [&](int r) {  // [P, B, S_q] index of query row r of this tile
+    return ((int64_t)p * desc.B + b) * desc.S_q + q0 + r;
+  };
+  auto lslot_of = [&](int r) {  // [P, B, H, S_q] index
+    return (((int64_t)p * desc.B + b) * H + head) * desc.S_q + q0 + r;
+  };
   if constexpr (FP8) {
     // compressed slot: e4m3 codes of O / s with s = max_d |O| / 448 per (row, head); the
     // lane pair holds the row's D values
+    constexpr int CPR8 = D / 16;  // 16-byte chunks (16 codes) per row
     float amax = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -448,41 +463,58 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
     amax = pair_max(amax);
     const float sc = amax / 448.f;
     const float inv_s = amax > 0.f ? 448.f / amax : 0.f;
-    if (qvalid) {
-      uint8_t *op = (uint8_t *)cache_o + (slot * H + head) * D;
-      const float old_s = is_local ? cache_scale[lslot] : 0.f;
+    float *stg_scale = (float *)(stg + 32 * D);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * db + 8 * g + 4 * hh;
-          float x[4];
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * hh;
+        float x[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) x[t] = (o[db][4 * g + t] * inv) * inv_s;
-          int wq = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-          wq = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wq, true);
-          if (is_local) {
-            const int od = *(const int *)(op + d0);
-            const f32x2 nv[2] = {__builtin_amdgcn_cvt_pk_f32_fp8(wq, false), __builtin_amdgcn_cvt_pk_f32_fp8(wq, true)};
-            const f32x2 ov[2] = {__builtin_amdgcn_cvt_pk_f32_fp8(od, false), __builtin_amdgcn_cvt_pk_f32_fp8(od, true)};
+        for (int t = 0; t < 4; ++t) x[t] = (o[db][4 * g + t] * inv) * inv_s;
+        int wq = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        wq = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wq, true);
+        *(int *)(stg + l32 * D + (((d0 >> 4) ^ (l32 % CPR8)) << 4) + (d0 & 15)) = wq;
+      }
+    }
+    if (hh == 0) stg_scale[l32] = sc;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float n0 = nv[t >> 1][t & 1] * sc;
-              const float o0 = ov[t >> 1][t & 1] * old_s;
+    for (int it = 0; it < 32 * CPR8 / 64; ++it) {
+      const int c = it * 64 + lane;
+      const int r = c / CPR8, col = c % CPR8;
+      const uint4 nw = *(const uint4 *)(stg + r * D + ((col ^ (r % CPR8)) << 4));
+      if (wave * 32 + r < qn) {
+        uint8_t *dst = (uint8_t *)cache_o + (slot_of(wave * 32 + r) * H + head) * D + col * 16;
+        if (is_local) {
+          const uint4 od = *(const uint4 *)dst;
+          const float old_s = cache_scale[lslot_of(wave * 32 + r)];
+          const float new_s = stg_scale[r];
+          const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w}, oo[4] = {od.x, od.y, od.z, od.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const f32x2 nv[2] = {__builtin_amdgcn_cvt_pk_f32_fp8((int)nn[t], false),
+                                 __builtin_amdgcn_cvt_pk_f32_fp8((int)nn[t], true)};
+            const f32x2 ov[2] = {__builtin_amdgcn_cvt_pk_f32_fp8((int)oo[t], false),
+                                 __builtin_amdgcn_cvt_pk_f32_fp8((int)oo[t], true)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float n0 = nv[e >> 1][e & 1] * new_s;
+              const float o0 = ov[e >> 1][e & 1] * old_s;
               dnum += (n0 - o0) * (n0 - o0);
               dden += o0 * o0;
             }
           }
-          *(int *)(op + d0) = wq;
         }
-      }
-      if (hh == 0) {
-        cache_lse[lslot] = lse_nat;
-        cache_scale[lslot] = sc;
+        *(uint4 *)dst = nw;
       }
     }
-  } else if (qvalid) {
-    u16 *op = (u16 *)cache_o + (slot * H + head) * D;
+    // after the old scales have been read above
+    if (qvalid && hh == 0) {
+      cache_lse[lslot_of(qrow)] = lse_nat;
+      cache_scale[lslot_of(qrow)] = sc;
+    }
+  } else {
+    constexpr int CPR = D / 8;  // 16-byte chunks (8 bf16) per row
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -491,21 +523,31 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
         uint2 nw;
         nw.x = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
         nw.y = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        if (is_local) {
-          const uint2 od = *(const uint2 *)(op + d0);
-          const uint32_t nn[2] = {nw.x, nw.y}, oo[2] = {od.x, od.y};
+        *(uint2 *)(stg + l32 * (2 * D) + (((d0 >> 3) ^ (l32 % CPR)) << 4) + (d0 & 7) * 2) = nw;
+      }
+    }
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+    for (int it = 0; it < 32 * CPR / 64; ++it) {
+      const int c = it * 64 + lane;
+      const int r = c / CPR, col = c % CPR;
+      const uint4 nw = *(const uint4 *)(stg + r * (2 * D) + ((col ^ (r % CPR)) << 4));
+      if (wave * 32 + r < qn) {
+        u16 *dst = (u16 *)cache_o + (slot_of(wave * 32 + r) * H + head) * D + col * 8;
+        if (is_local) {
+          const uint4 od = *(const uint4 *)dst;
+          const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w}, oo[4] = {od.x, od.y, od.z, od.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
             const float n0 = bf16_bits_to_f32(nn[t] & 0xffffu), n1 = bf16_bits_to_f32(nn[t] >> 16);
             const float o0 = bf16_bits_to_f32(oo[t] & 0xffffu), o1 = bf16_bits_to_f32(oo[t] >> 16);
             dnum += (n0 - o0) * (n0 - o0) + (n1 - o1) * (n1 - o1);
             dden += o0 * o0 + o1 * o1;
           }
         }
-        *(uint2 *)(op + d0) = nw;
+        *(uint4 *)dst = nw;
       }
     }
-    if (hh == 0) cache_lse[lslot] = lse_nat;
+    if (qvalid && hh == 0) cache_lse[lslot_of(qrow)] = lse_nat;
   }
   if (is_local) {
 #pragma unroll
