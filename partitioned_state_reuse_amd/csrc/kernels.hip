@@ -7,6 +7,7 @@
 // (O_p, lse_p) is produced; the states are composed by LSE-weighted combination.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "launch.h"
@@ -575,6 +576,26 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   }
 }
 
+// Workgroups are dealt round-robin to the 8 XCDs (workgroup w runs on XCD w mod 8), and
+// each XCD has its own L2.  The merge kernels take row-heads in (row, head) order while
+// the lse (and scale) planes are [head][row], so one lse line serves the same heads of
+// several consecutive rows, i.e. a run of consecutive workgroups.  Remap so that each XCD
+// takes runs of `chunk` consecutive workgroups (each lse line is fetched into one L2),
+// while the 8 XCDs still stream neighbouring runs at the same time.  The ragged tail keeps
+// the identity mapping.
+__device__ __forceinline__ int lse_chunked_item(int chunk) {
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int span = 8 * chunk;
+  const int base = (wg / span) * span;
+  if (chunk <= 1 || base + span > nwg) return wg;
+  const int r = wg - base;
+  return base + (r & 7) * chunk + (r >> 3);
+}
+
+// Workgroups per XCD run of the merge kernels: those covering kMergeChunkRows rows of all
+// H heads (RPW row-heads per workgroup).
+inline int merge_chunk(int RPW, int H) { return std::max(1, kMergeChunkRows * H / RPW); }
+
 // ------------------------------------------------------------------------------------
 // State merge: one thread per 8 consecutive d of one (row, head), a workgroup per 16
 // consecutive row-heads (4 KB contiguous runs of every partition plane); all P lse values
@@ -586,10 +607,10 @@ template <int D, int PMAX>
 __global__ __launch_bounds__(256) void state_merge_kernel(
     const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, u16 *__restrict__ out,
     float *__restrict__ lse_out, const int S_q, const int H, const int P, const int64_t total_rh,
-    const int64_t plane_o, const int64_t plane_lse) {
+    const int64_t plane_o, const int64_t plane_lse, const int chunk) {
   constexpr int TPR = D / 8;
   constexpr int RPW = 256 / TPR;
-  const int64_t rh = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const int64_t rh = (int64_t)lse_chunked_item(chunk) * RPW + threadIdx.x / TPR;
   if (rh >= total_rh) return;
   const int c = threadIdx.x % TPR;
   const int64_t br = rh / H;  // b * S_q + r
@@ -646,11 +667,11 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
     const uint8_t *__restrict__ cache_q8, const float *__restrict__ cache_scale,
     const float *__restrict__ cache_lse, u16 *__restrict__ out, float *__restrict__ lse_out,
     const int S_q, const int H, const int P, const int64_t total_rh, const int64_t plane_o,
-    const int64_t plane_lse) {
+    const int64_t plane_lse, const int chunk) {
   constexpr int TPR = D / kFp8Dpt;
   constexpr int RPW = 256 / TPR;
   constexpr int NW = kFp8Dpt / 4;  // 32-bit code words per thread and plane
-  const int64_t rh = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const int64_t rh = (int64_t)lse_chunked_item(chunk) * RPW + threadIdx.x / TPR;
   if (rh >= total_rh) return;
   const int c = threadIdx.x % TPR;
   const int64_t br = rh / H;
@@ -723,17 +744,18 @@ hipError_t merge_fp8_dispatch(int P, const void *cache_q8, const float *cache_sc
   const int64_t nwg = (total_rh + RPW - 1) / RPW;
   const int64_t plane_o = total_rh * D;
   const int64_t plane_lse = total_rh;
+  const int chunk = merge_chunk(RPW, H);
   dim3 grid((unsigned)nwg), block(256);
   const uint8_t *cq = (const uint8_t *)cache_q8;
   u16 *oo = (u16 *)out;
   if (P <= 8)
-    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 8>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 8>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else if (P <= 16)
-    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 16>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 16>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else if (P <= 32)
-    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 32>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 32>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else
-    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 64>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 64>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   return hipGetLastError();
 }
 
@@ -746,10 +768,10 @@ __global__ __launch_bounds__(256) void state_merge_masked_kernel(
     const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, const u16 *__restrict__ extra_o,
     const float *__restrict__ extra_lse, const MergeSelect sel, u16 *__restrict__ out,
     float *__restrict__ lse_out, const int S_q, const int H, const int P, const int64_t total_rh,
-    const int64_t plane_o, const int64_t plane_lse) {
+    const int64_t plane_o, const int64_t plane_lse, const int chunk) {
   constexpr int TPR = D / 8;
   constexpr int RPW = 256 / TPR;
-  const int64_t rh = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const int64_t rh = (int64_t)lse_chunked_item(chunk) * RPW + threadIdx.x / TPR;
   if (rh >= total_rh) return;
   const int c = threadIdx.x % TPR;
   const int64_t br = rh / H;
@@ -818,18 +840,19 @@ hipError_t merge_masked_dispatch(int P, const void *cache_o, const float *cache_
   const int64_t nwg = (total_rh + RPW - 1) / RPW;
   const int64_t plane_o = total_rh * D;
   const int64_t plane_lse = total_rh;
+  const int chunk = merge_chunk(RPW, H);
   dim3 grid((unsigned)nwg), block(256);
   const u16 *co = (const u16 *)cache_o;
   const u16 *eo = (const u16 *)extra_o;
   u16 *oo = (u16 *)out;
   if (P <= 8)
-    hipLaunchKernelGGL((state_merge_masked_kernel<D, 8>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_masked_kernel<D, 8>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else if (P <= 16)
-    hipLaunchKernelGGL((state_merge_masked_kernel<D, 16>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_masked_kernel<D, 16>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else if (P <= 32)
-    hipLaunchKernelGGL((state_merge_masked_kernel<D, 32>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_masked_kernel<D, 32>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else
-    hipLaunchKernelGGL((state_merge_masked_kernel<D, 64>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_masked_kernel<D, 64>), grid, block, 0, stream, co, cache_lse, eo, extra_lse, sel, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   return hipGetLastError();
 }
 
@@ -900,17 +923,18 @@ hipError_t merge_dispatch(int P, const void *cache_o, const float *cache_lse, vo
   const int64_t nwg = (total_rh + RPW - 1) / RPW;
   const int64_t plane_o = total_rh * D;
   const int64_t plane_lse = total_rh;
+  const int chunk = merge_chunk(RPW, H);
   dim3 grid((unsigned)nwg), block(256);
   const u16 *co = (const u16 *)cache_o;
   u16 *oo = (u16 *)out;
   if (P <= 8)
-    hipLaunchKernelGGL((state_merge_kernel<D, 8>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_kernel<D, 8>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else if (P <= 16)
-    hipLaunchKernelGGL((state_merge_kernel<D, 16>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_kernel<D, 16>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else if (P <= 32)
-    hipLaunchKernelGGL((state_merge_kernel<D, 32>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_kernel<D, 32>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   else
-    hipLaunchKernelGGL((state_merge_kernel<D, 64>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse);
+    hipLaunchKernelGGL((state_merge_kernel<D, 64>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
   return hipGetLastError();
 }
 

@@ -30,6 +30,11 @@ constexpr int kStages = DIT_ATTN_STAGES;    // K/V tile buffers in the LDS ring 
 #endif
 // raise the wave priority while it issues MFMAs (K Q^T and V^T P^T), lower it for the softmax
 constexpr bool kSetPrio = DIT_ATTN_SETPRIO != 0;
+#ifndef DIT_MERGE_CHUNK_ROWS
+#define DIT_MERGE_CHUNK_ROWS 16
+#endif
+// query rows (of all heads) whose merge workgroups run on one XCD in a row (0: round-robin)
+constexpr int kMergeChunkRows = DIT_MERGE_CHUNK_ROWS;
 #ifndef DIT_MERGE_FP8_DPT
 #define DIT_MERGE_FP8_DPT 16
 #endif
