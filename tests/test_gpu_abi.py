@@ -1,0 +1,160 @@
+"""GPU checks of the C ABI's contract beyond numerics:
+
+  - a call that fails validation enqueues nothing: every output buffer, filled with a
+    sentinel beforehand, is bitwise unchanged afterwards (for each entry point and each
+    class of error);
+  - results are deterministic: repeating a step from the same cache state gives bitwise
+    equal outputs, cache slots, importance and local change (fixed-order reductions, no
+    floating-point atomics), for the bf16 and the fp8 cache, the masked merge and the
+    group compose.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import workloads as W
+import _parity as PT
+from partitioned_state_reuse_amd import api
+
+pytestmark = pytest.mark.gpu
+
+
+def _sentinel(t: torch.Tensor) -> torch.Tensor:
+    t.view(torch.uint8).fill_(0xA5)
+    return t
+
+
+class Bufs:
+    """Every output buffer of one workload, sentinel-filled."""
+
+    def __init__(self, w, fp8=False):
+        P, n_qb, S_q, H, D = w.P, w.n_qb, w.S_q, w.H, w.D
+        dt = torch.uint8 if fp8 else torch.bfloat16
+        self.cache_o = _sentinel(torch.empty((P, 1, S_q, H, D), dtype=dt, device="cuda"))
+        self.cache_scale = _sentinel(torch.empty((P, 1, H, S_q), dtype=torch.float32, device="cuda"))
+        self.cache_lse = _sentinel(torch.empty((P, 1, H, S_q), dtype=torch.float32, device="cuda"))
+        self.out = _sentinel(torch.empty((1, S_q, H, D), dtype=torch.bfloat16, device="cuda"))
+        self.lse = _sentinel(torch.empty((1, H, S_q), dtype=torch.float32, device="cuda"))
+        self.imp = _sentinel(torch.empty((1, n_qb, P), dtype=torch.float32, device="cuda"))
+        self.delta = _sentinel(torch.empty((1, n_qb), dtype=torch.float32, device="cuda"))
+        nb = api.workspace_bytes(1, S_q, H, D, n_qb, P)
+        self.ws = _sentinel(torch.empty(max(nb, 4) // 4, dtype=torch.float32, device="cuda"))
+        self.comp_o = _sentinel(torch.empty((1, 1, S_q, H, D), dtype=torch.bfloat16, device="cuda"))
+        self.comp_l = _sentinel(torch.empty((1, 1, H, S_q), dtype=torch.float32, device="cuda"))
+
+    def snapshot(self):
+        torch.cuda.synchronize()
+        return {k: v.clone() for k, v in vars(self).items()}
+
+    def unchanged(self, snap):
+        torch.cuda.synchronize()
+        return [k for k, v in vars(self).items() if not torch.equal(v.view(torch.uint8), snap[k].view(torch.uint8))]
+
+
+def _inputs(w):
+    X = W.make_step(w, 0)
+    return PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
+
+
+def test_rejected_calls_touch_no_buffer():
+    w = W.workload("video720p", grid=(3, 12, 20), H=2)
+    q, k, v = _inputs(w)
+    ones = np.ones((w.n_qb, w.P), np.uint8)
+    b = Bufs(w)
+    snap = b.snapshot()
+    bad_qo = list(w.q_offsets)
+    bad_qo[1] = bad_qo[2]                                  # empty query block
+    bad_ko = list(w.kv_offsets)
+    bad_ko[-1] -= 1                                        # does not end at S_kv
+    no_local = ones.copy()
+    no_local[0, w.local_part[0]] = 0                       # local partition not recomputed
+    reuse_invalid = ones.copy()
+    reuse_invalid[0, (w.local_part[0] + 1) % w.P] = 0      # reuse of a never-computed slot
+    calls = [
+        (-3, lambda: api.attn_partitioned(q, k, v, bad_qo, w.kv_offsets, ones, b.cache_o, b.cache_lse, b.out, b.lse,
+                                          local_part=w.local_part)),
+        (-3, lambda: api.attn_partitioned(q, k, v, w.q_offsets, bad_ko, ones, b.cache_o, b.cache_lse, b.out, b.lse,
+                                          local_part=w.local_part)),
+        (-4, lambda: api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, no_local, b.cache_o, b.cache_lse,
+                                          b.out, b.lse, local_part=w.local_part)),
+        (-5, lambda: api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, reuse_invalid, b.cache_o, b.cache_lse,
+                                          b.out, b.lse, local_part=w.local_part,
+                                          cache_valid=np.zeros((w.n_qb, w.P), np.uint8))),
+        (-6, lambda: api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, ones, b.cache_o, b.cache_lse, b.out,
+                                          b.lse, local_part=w.local_part, delta_out=b.delta,
+                                          workspace=b.ws[:1], importance_out=b.imp)),
+        (-3, lambda: api.partition_attention(q, k, v, bad_qo, w.kv_offsets, ones, b.cache_o, b.cache_lse)),
+        (-4, lambda: api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, ones * 2, b.cache_o, b.cache_lse)),
+        (-3, lambda: api.importance(b.cache_lse, b.lse, bad_qo, b.imp)),
+        (-6, lambda: api.local_change_finalize(b.ws[:1], 1, w.S_q, w.H, w.D, w.q_offsets, b.delta)),
+        (-3, lambda: api.state_compose(b.cache_o, b.cache_lse, [0, w.P - 1], b.comp_o, b.comp_l)),
+        (-3, lambda: api.state_merge_masked(b.cache_o, b.cache_lse, bad_qo, ones, b.out, b.lse)),
+        (-4, lambda: api.state_merge_masked(b.cache_o, b.cache_lse, w.q_offsets, ones * 3, b.out, b.lse)),
+    ]
+    for i, (code, fn) in enumerate(calls):
+        with pytest.raises(api.DitError) as e:
+            fn()
+        assert e.value.code == code, (i, e.value.code, code)
+        changed = b.unchanged(snap)
+        assert not changed, (i, changed)
+
+
+def test_rejected_fp8_calls_touch_no_buffer():
+    w = W.workload("tiny")
+    q, k, v = _inputs(w)
+    b = Bufs(w, fp8=True)
+    snap = b.snapshot()
+    ones = np.ones((w.n_qb, w.P), np.uint8)
+    bad_ko = [0, 64, 32, 192, 256]
+    with pytest.raises(api.DitError) as e:
+        api.partition_attention_fp8(q, k, v, w.q_offsets, bad_ko, ones, b.cache_o, b.cache_scale, b.cache_lse)
+    assert e.value.code == -3
+    with pytest.raises(api.DitError) as e:
+        api.partition_attention_fp8(q, k, v, w.q_offsets, w.kv_offsets, ones, b.cache_o, None, b.cache_lse)
+    assert e.value.code == -1
+    assert not b.unchanged(snap)
+
+
+def _step_outputs(sa):
+    torch.cuda.synchronize()
+    outs = [sa.out, sa.lse, sa.cache_o, sa.cache_lse, sa.importance, sa.delta]
+    if sa.cache_scale is not None:
+        outs.append(sa.cache_scale)
+    return [t.clone() for t in outs]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_repeated_step_is_bitwise_identical(fmt):
+    w = W.workload("video720p", grid=(5, 18, 32), H=3)
+    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
+    ones = np.ones((w.n_qb, w.P), np.uint8)
+    mask, _, _, _ = PT.masks_from_planners(w)
+    runs = []
+    for _ in range(2):
+        sa = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part,
+                                    cache_format=fmt)
+        sa.step(PT.to_dev(Xp.q), PT.to_dev(Xp.k), PT.to_dev(Xp.v), ones)
+        did = sa.step(PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v), mask, want_importance=True, want_delta=True)
+        assert did
+        runs.append(_step_outputs(sa))
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_masked_merge_and_compose_are_bitwise_repeatable():
+    w = W.workload("video720p", grid=(3, 12, 20), H=2)
+    q, k, v = _inputs(w)
+    sa = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part)
+    sa.step(q, k, v, np.ones((w.n_qb, w.P), np.uint8))
+    sel = (np.arange(w.n_qb * w.P).reshape(w.n_qb, w.P) % 3 != 0).astype(np.uint8)
+    res = []
+    for _ in range(2):
+        o = torch.empty_like(sa.out)
+        l = torch.empty_like(sa.lse)
+        api.state_merge_masked(sa.cache_o, sa.cache_lse, w.q_offsets, sel, o, l)
+        c = sa.compose(w.group_offsets)
+        torch.cuda.synchronize()
+        res.append((o, l, c.cache_o.clone(), c.cache_lse.clone()))
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
