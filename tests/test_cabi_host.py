@@ -85,6 +85,49 @@ def test_too_many_blocks_or_partitions(L):
     assert _call(L, S_kv=65, ko=ko, rec=[1] + [0] * 64) == -2
 
 
+def _i32(s):
+    return None if s is None else (ctypes.c_int32 * len(s))(*s)
+
+
+def _u8(s):
+    return None if s is None else (ctypes.c_uint8 * len(s))(*s)
+
+
+@pytest.mark.parametrize("call,code", [
+    # dit_partition_attention_fp8(q, k, v, B, S_q, S_kv, H, D, qo, n_qb, ko, P, local, rec, q8, scale, lse, sm, ws, wsb, st)
+    (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
+                                             _u8([1, 0]), 1, None, 1, 0.0, None, 0, None), -1),
+    (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 96, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
+                                             _u8([1, 0]), 1, 1, 1, 0.0, None, 0, None), -7),
+    (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 5, 4]), 2, _i32([0]),
+                                             _u8([1, 0]), 1, 1, 1, 0.0, None, 0, None), -3),
+    (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
+                                             _u8([0, 1]), 1, 1, 1, 0.0, None, 0, None), -4),
+    # dit_state_merge_fp8(q8, scale, lse, B, S_q, H, D, P, out, lse_out, st)
+    (lambda L: L.dit_state_merge_fp8(1, None, 1, 1, 8, 1, 64, 2, 1, 1, None), -1),
+    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 64, 65, 1, 1, None), -2),
+    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 48, 2, 1, 1, None), -7),
+    # dit_state_merge(o, lse, B, S_q, H, D, P, out, lse_out, st)
+    (lambda L: L.dit_state_merge(1, 1, 1, 8, 1, 64, 0, 1, 1, None), -2),
+    (lambda L: L.dit_state_merge(1, None, 1, 8, 1, 64, 2, 1, 1, None), -1),
+    # dit_state_merge_masked(o, lse, B, S_q, H, D, P, qo, n_qb, sel, extra_o, extra_lse, out, lse_out, st)
+    (lambda L: L.dit_state_merge_masked(1, 1, 1, 8, 1, 64, 2, _i32([0, 8]), 1, _u8([1, 2]), None, None, 1, 1, None), -4),
+    (lambda L: L.dit_state_merge_masked(1, 1, 1, 8, 1, 64, 2, _i32([0, 9]), 1, _u8([1, 0]), None, None, 1, 1, None), -3),
+    (lambda L: L.dit_state_merge_masked(1, 1, 1, 8, 1, 64, 2, _i32([0, 8]), 1, _u8([1, 0]), 1, None, 1, 1, None), -1),
+    # dit_state_compose(o, lse, P_in, go, G, B, S_q, H, D, out_o, out_lse, st)
+    (lambda L: L.dit_state_compose(1, 1, 4, _i32([0, 2, 2, 4]), 3, 1, 8, 1, 64, 1, 1, None), -3),
+    (lambda L: L.dit_state_compose(1, 1, 4, _i32([0, 2, 3]), 2, 1, 8, 1, 64, 1, 1, None), -3),
+    (lambda L: L.dit_state_compose(1, 1, 4, _i32([0, 1, 2, 3, 4, 4]), 5, 1, 8, 1, 64, 1, 1, None), -2),
+    (lambda L: L.dit_state_compose(1, 1, 4, _i32([0, 4]), 1, 1, 8, 1, 80, 1, 1, None), -7),
+    # dit_importance(clse, lse, B, S_q, H, P, qo, n_qb, imp, st) and dit_local_change_finalize
+    (lambda L: L.dit_importance(1, 1, 1, 8, 1, 2, _i32([0, 4, 4, 8]), 3, 1, None), -3),
+    (lambda L: L.dit_local_change_finalize(1, 4, 1, 8, 1, 64, _i32([0, 8]), 1, 1, None), -6),
+], ids=lambda x: "" if callable(x) else str(x))
+def test_other_entry_points_validate_before_launch(L, call, code):
+    """Each error is caught on the host (fake device pointers are never dereferenced)."""
+    assert call(L) == code
+
+
 # ----------------------------------------------------------------------------- planner
 
 from partitioned_state_reuse_amd.api import Planner, DitError  # noqa: E402
