@@ -1,0 +1,27 @@
+"""CPU checks of bench.py's command-line contract (nothing here touches a GPU)."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_traffic_record_matches_kernel_sources_or_is_ignored():
+    """The committed HBM-traffic record is used only while its source hash matches."""
+    sys.path.insert(0, ROOT)
+    import bench
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_video720p.json")))
+    got = bench.measured_traffic("video720p")
+    if rec["source_sha256"] == bench.kernel_source_sha256():
+        assert got and all(v > 0 for v in got.values())
+    else:
+        assert got == {}
