@@ -598,11 +598,57 @@ inline int merge_chunk(int RPW, int H) { return std::max(1, kMergeChunkRows * H 
 
 // ------------------------------------------------------------------------------------
 // State merge: one thread per 8 consecutive d of one (row, head), a workgroup per 16
-// consecutive row-heads (4 KB contiguous runs of every partition plane); all P lse values
-// of the row-head are kept in registers (PMAX >= P, unrolled), then the P bf16 states are
-// streamed with 16-byte non-temporal loads and combined in fp32; the merged output is
+// consecutive row-heads (4 KB contiguous runs of every partition plane).  The row-head's
+// lanes first share out the merge weights (group_merge_weights: each lse value is loaded
+// by one lane, not by all of them), then the P bf16 states are streamed with 16-byte
+// non-temporal loads (PMAX >= P, unrolled) and combined in fp32; the merged output is
 // written with non-temporal stores (it is not re-read by this step).
 // ------------------------------------------------------------------------------------
+// Merge weights of one row-head, computed by the TPR lanes that share it (one wave holds
+// whole groups): lane c loads the lse (and, with SCALED, the scale) of planes c, c + TPR,
+// ... only; the maximum and the sum of exponentials are reduced over the group with an xor
+// butterfly (every lane ends with the same values, in a fixed order); the weights
+// w_p = e^{lse_p - lse} (times s_p) go to wts[0 .. PMAX) in LDS, where every lane of the
+// group reads them.  Planes at or past P, and empty states, get weight 0.  Returns the
+// merged lse (-inf when every state is empty).
+template <int TPR, int PMAX, bool SCALED>
+__device__ __forceinline__ float group_merge_weights(const float *__restrict__ cache_lse,
+                                                     const float *__restrict__ cache_scale, int64_t li,
+                                                     int64_t plane_lse, int P, int c, float *wts) {
+  constexpr int NPL = (PMAX + TPR - 1) / TPR;
+  float lv[NPL];
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int p = c + TPR * k;
+    lv[k] = (p < P) ? cache_lse[p * plane_lse + li] : -INFINITY;
+    M = fmaxf(M, lv[k]);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) sum += (lv[k] > -INFINITY) ? __expf(lv[k] - M) : 0.f;
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  const float L = (M > -INFINITY) ? M + __logf(sum) : -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int p = c + TPR * k;
+    if (p < PMAX) {
+      float w = (lv[k] > -INFINITY) ? __expf(lv[k] - L) : 0.f;
+      if constexpr (SCALED) w = (p < P) ? w * cache_scale[p * plane_lse + li] : 0.f;
+      wts[p] = w;
+    }
+  }
+  // the group's lanes are in this wave: LDS accesses of one wave complete in order, and
+  // the barrier keeps the compiler from moving the readers' loads above these stores
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return L;
+}
+
 template <int D, int PMAX>
 __global__ __launch_bounds__(256) void state_merge_kernel(
     const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, u16 *__restrict__ out,
@@ -619,18 +665,9 @@ __global__ __launch_bounds__(256) void state_merge_kernel(
   const int64_t r = br - b * S_q;
   const int64_t li = (b * H + h) * S_q + r;
 
-  float lv[PMAX];
-  float M = -INFINITY;
-#pragma unroll
-  for (int p = 0; p < PMAX; ++p) {
-    lv[p] = (p < P) ? cache_lse[p * plane_lse + li] : -INFINITY;
-    M = fmaxf(M, lv[p]);
-  }
-  const bool any = M > -INFINITY;
-  float sum = 0.f;
-#pragma unroll
-  for (int p = 0; p < PMAX; ++p) sum += (lv[p] > -INFINITY) ? __expf(lv[p] - M) : 0.f;
-  const float L = any ? M + __logf(sum) : -INFINITY;
+  __shared__ float wts_all[RPW][PMAX];
+  float *wts = wts_all[threadIdx.x / TPR];
+  const float L = group_merge_weights<TPR, PMAX, false>(cache_lse, nullptr, li, plane_lse, P, c, wts);
 
   float acc[8];
 #pragma unroll
@@ -639,7 +676,7 @@ __global__ __launch_bounds__(256) void state_merge_kernel(
 #pragma unroll
   for (int p = 0; p < PMAX; ++p) {
     if (p < P) {
-      const float w = (lv[p] > -INFINITY) ? __expf(lv[p] - L) : 0.f;
+      const float w = wts[p];
       const u32x4 u = __builtin_nontemporal_load((const u32x4 *)(src + p * plane_o));
       const uint32_t x[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
@@ -680,18 +717,9 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
   const int64_t r = br - b * S_q;
   const int64_t li = (b * H + h) * S_q + r;
 
-  float lv[PMAX];
-  float M = -INFINITY;
-#pragma unroll
-  for (int p = 0; p < PMAX; ++p) {
-    lv[p] = (p < P) ? cache_lse[p * plane_lse + li] : -INFINITY;
-    M = fmaxf(M, lv[p]);
-  }
-  const bool any = M > -INFINITY;
-  float sum = 0.f;
-#pragma unroll
-  for (int p = 0; p < PMAX; ++p) sum += (lv[p] > -INFINITY) ? __expf(lv[p] - M) : 0.f;
-  const float L = any ? M + __logf(sum) : -INFINITY;
+  __shared__ float wts_all[RPW][PMAX];
+  float *wts = wts_all[threadIdx.x / TPR];
+  const float L = group_merge_weights<TPR, PMAX, true>(cache_lse, cache_scale, li, plane_lse, P, c, wts);
 
   float acc[kFp8Dpt];
 #pragma unroll
@@ -700,7 +728,7 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
 #pragma unroll
   for (int p = 0; p < PMAX; ++p) {
     if (p < P) {
-      const float w = (lv[p] > -INFINITY) ? __expf(lv[p] - L) * cache_scale[p * plane_lse + li] : 0.f;
+      const float w = wts[p];
       uint32_t u[NW];
       if constexpr (NW >= 4) {
 #pragma unroll
