@@ -41,16 +41,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // ------------------------------------------------------------------------------------
 // Partition attention.
 //
-// One workgroup = 8 waves (two per SIMD) = one (batch, head, partition p, query tile of
-// <= 256 rows of one query block); a wave whose 32 rows all lie past the block end only
-// helps with the tile copies.  Each wave owns 32 query rows and keeps them in registers as the B
-// operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so that each lane's 16 scores per
-// 32-key block belong to one query and the softmax reductions over keys stay inside a
-// lane pair (l, l ^ 32), joined with v_permlane32_swap.
+// One workgroup = kWaves waves (default 4; 3 workgroups per CU, i.e. 3 waves per SIMD) =
+// one (batch, head, partition p, query tile of <= 32 kWaves rows of one query block); a
+// wave whose 32 rows all lie past the block end only helps with the tile copies.  Each wave
+// owns 32 query rows and keeps them in registers as the B operand of S^T = K Q^T
+// (v_mfma_f32_32x32x16_bf16), so that each lane's 16 scores per 32-key block belong to one
+// query and the softmax reductions over keys stay inside a lane pair (l, l ^ 32), joined
+// with v_permlane32_swap.
 //
-// K and V tiles of 64 keys are copied global -> LDS by the DMA path
-// (global_load_lds_dwordx4, no VGPR staging), double-buffered so that the next tile is in
-// flight while the current one is consumed.  Both tiles stay row-major [key][d] with a
+// K and V tiles of kBlockN keys (default 32) are copied global -> LDS by the DMA path
+// (global_load_lds_dwordx4, no VGPR staging) into a ring of kStages buffers (default 2) so
+// that the next tile is in flight while the current one is consumed.  Both tiles stay
+// row-major [key][d] with a
 // per-row XOR swizzle of the 16-byte chunks, chosen so that the K reads (ds_read_b128, A
 // operand of K Q^T) and the V reads are free of bank conflicts.  V^T, the A operand of
 // O^T = V^T P^T, is read with the LDS transpose load ds_read_b64_tr_b16: in each group of
@@ -64,7 +66,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // for the exponentials is raised only when a tile's maximum exceeds it by more than
 // kRescaleLog2 (then exponentials stay <= 2^kRescaleLog2 and nothing overflows), which
 // skips the rescale of the accumulators on almost every tile.  P is rounded to bf16 for
-// the product.  The epilogue writes the partition's state into its cache slot and, for a
+// the product.  The epilogue writes the partition's state into its cache slot (bf16, or
+// e4m3 codes plus a per-row scale with FP8) through an LDS staging buffer and, for a
 // block's local partition, the partial sums of the local-change norm.
 // ------------------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.0f;
@@ -896,28 +899,50 @@ __device__ __forceinline__ float block_sum_256(float x, float *sh) {
   return sh[0];
 }
 
-// Importance: one workgroup per (batch, block i, partition p).
-__global__ __launch_bounds__(256) void importance_kernel(
+// Importance: one workgroup of 1024 threads per (batch, block i, partition p).  Each thread
+// walks the block's rows of every head with four independent loads in flight (rows r,
+// r + 1024, r + 2048, r + 3072), then a fixed-order tree sums the threads.
+constexpr int kImpThreads = 1024;
+__device__ __forceinline__ float block_sum_1024(float x, float *sh) {
+  sh[threadIdx.x] = x;
+  __syncthreads();
+#pragma unroll
+  for (int s = kImpThreads / 2; s >= 1; s >>= 1) {
+    if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
+    __syncthreads();
+  }
+  return sh[0];
+}
+
+__global__ __launch_bounds__(kImpThreads) void importance_kernel(
     const float *__restrict__ cache_lse, const float *__restrict__ lse, const int S_q, const int H,
     const int P, const int B, const BlockDesc blocks, float *__restrict__ out) {
-  __shared__ float sh[256];
+  __shared__ float sh[kImpThreads];
   const int p = blockIdx.x % P;
   const int i = blockIdx.x / P;
   const int b = blockIdx.y;
   const int r0 = blocks.q_off[i];
   const int nr = blocks.q_off[i + 1] - r0;
-  const int64_t n = (int64_t)nr * H;
-  const float *cl = cache_lse + ((int64_t)p * B + b) * H * S_q;
-  const float *ml = lse + (int64_t)b * H * S_q;
-  float acc = 0.f;
-  for (int64_t e = threadIdx.x; e < n; e += 256) {
-    const int h = (int)(e / nr);
-    const int r = r0 + (int)(e - (int64_t)h * nr);
-    const float a = cl[(int64_t)h * S_q + r];
-    const float t = ml[(int64_t)h * S_q + r];
-    acc += (a > -INFINITY && t > -INFINITY) ? __expf(a - t) : 0.f;
+  const float *cl = cache_lse + ((int64_t)p * B + b) * H * S_q + r0;
+  const float *ml = lse + (int64_t)b * H * S_q + r0;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < H; ++h) {
+    const float *clh = cl + (int64_t)h * S_q;
+    const float *mlh = ml + (int64_t)h * S_q;
+    for (int r = threadIdx.x; r < nr; r += 4 * kImpThreads) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rr = r + u * kImpThreads;
+        if (rr < nr) {
+          const float a = clh[rr];
+          const float t = mlh[rr];
+          acc[u] += (a > -INFINITY && t > -INFINITY) ? __expf(a - t) : 0.f;
+        }
+      }
+    }
   }
-  const float tot = block_sum_256(acc, sh);
+  const float tot = block_sum_1024((acc[0] + acc[1]) + (acc[2] + acc[3]), sh);
+  const int64_t n = (int64_t)nr * H;
   if (threadIdx.x == 0) out[((int64_t)b * blocks.n_qb + i) * P + p] = n > 0 ? tot / (float)n : 0.f;
 }
 
@@ -1018,7 +1043,7 @@ hipError_t launch_state_merge_masked(int D, int P, const void *cache_o, const fl
 hipError_t launch_importance(const float *cache_lse, const float *lse, int B, int S_q, int H, int P,
                              const BlockDesc &blocks, float *importance_out, hipStream_t stream) {
   (void)hipGetLastError();
-  dim3 grid((unsigned)(blocks.n_qb * P), (unsigned)B), block(256);
+  dim3 grid((unsigned)(blocks.n_qb * P), (unsigned)B), block(kImpThreads);
   hipLaunchKernelGGL(importance_kernel, grid, block, 0, stream, cache_lse, lse, S_q, H, P, B, blocks,
                      importance_out);
   return hipGetLastError();
