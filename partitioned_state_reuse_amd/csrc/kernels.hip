@@ -612,24 +612,30 @@ inline int merge_chunk(int RPW, int H) { return std::max(1, kMergeChunkRows * H 
 // ... only; the maximum and the sum of exponentials are reduced over the group with an xor
 // butterfly (every lane ends with the same values, in a fixed order); the weights
 // w_p = e^{lse_p - lse} (times s_p) go to wts[0 .. PMAX) in LDS, where every lane of the
-// group reads them.  Planes at or past P, and empty states, get weight 0.  Returns the
-// merged lse (-inf when every state is empty).
+// group reads them.  Planes at or past P, planes outside the mask `pm` and empty states get
+// weight 0.  An extra state (extra_lse non-null, lse loaded by lane 0) takes part in the
+// merge with its weight in wts[PMAX].  Returns the merged lse (-inf when every state is
+// empty).
 template <int TPR, int PMAX, bool SCALED>
 __device__ __forceinline__ float group_merge_weights(const float *__restrict__ cache_lse,
                                                      const float *__restrict__ cache_scale, int64_t li,
-                                                     int64_t plane_lse, int P, int c, float *wts) {
+                                                     int64_t plane_lse, int P, int c, float *wts,
+                                                     uint64_t pm = ~0ull,
+                                                     const float *__restrict__ extra_lse = nullptr) {
   constexpr int NPL = (PMAX + TPR - 1) / TPR;
   float lv[NPL];
   float M = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
     const int p = c + TPR * k;
-    lv[k] = (p < P) ? cache_lse[p * plane_lse + li] : -INFINITY;
+    lv[k] = (p < P && ((pm >> p) & 1)) ? cache_lse[p * plane_lse + li] : -INFINITY;
     M = fmaxf(M, lv[k]);
   }
+  const float lx = (extra_lse != nullptr && c == 0) ? extra_lse[li] : -INFINITY;
+  M = fmaxf(M, lx);
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float sum = 0.f;
+  float sum = (lx > -INFINITY) ? __expf(lx - M) : 0.f;
 #pragma unroll
   for (int k = 0; k < NPL; ++k) sum += (lv[k] > -INFINITY) ? __expf(lv[k] - M) : 0.f;
 #pragma unroll
@@ -644,6 +650,7 @@ __device__ __forceinline__ float group_merge_weights(const float *__restrict__ c
       wts[p] = w;
     }
   }
+  if (extra_lse != nullptr && c == 0) wts[PMAX] = (lx > -INFINITY) ? __expf(lx - L) : 0.f;
   // the group's lanes are in this wave: LDS accesses of one wave complete in order, and
   // the barrier keeps the compiler from moving the readers' loads above these stores
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -818,40 +825,27 @@ __global__ __launch_bounds__(256) void state_merge_masked_kernel(
   }
   const uint64_t pm = sel.plane_mask[lo];
 
-  float lv[PMAX + 1];
-  float M = -INFINITY;
-#pragma unroll
-  for (int p = 0; p < PMAX; ++p) {
-    lv[p] = (p < P && ((pm >> p) & 1)) ? cache_lse[p * plane_lse + li] : -INFINITY;
-    M = fmaxf(M, lv[p]);
-  }
-  lv[PMAX] = sel.has_extra ? extra_lse[li] : -INFINITY;
-  M = fmaxf(M, lv[PMAX]);
-  const bool any = M > -INFINITY;
-  float sum = 0.f;
-#pragma unroll
-  for (int p = 0; p <= PMAX; ++p) sum += (lv[p] > -INFINITY) ? __expf(lv[p] - M) : 0.f;
-  const float L = any ? M + __logf(sum) : -INFINITY;
+  __shared__ float wts_all[RPW][PMAX + 1];
+  float *wts = wts_all[threadIdx.x / TPR];
+  const float L = group_merge_weights<TPR, PMAX, false>(cache_lse, nullptr, li, plane_lse, P, c, wts, pm,
+                                                        sel.has_extra ? extra_lse : nullptr);
 
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  auto add = [&](const u16 *src, float lp) {
-    if (lp > -INFINITY) {
-      const float w = __expf(lp - L);
-      const u32x4 u = __builtin_nontemporal_load((const u32x4 *)src);
+  auto add = [&](const u16 *src, float w) {
+    const u32x4 u = __builtin_nontemporal_load((const u32x4 *)src);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        acc[2 * t] += w * bf16_bits_to_f32(u[t] & 0xffffu);
-        acc[2 * t + 1] += w * bf16_bits_to_f32(u[t] >> 16);
-      }
+    for (int t = 0; t < 4; ++t) {
+      acc[2 * t] += w * bf16_bits_to_f32(u[t] & 0xffffu);
+      acc[2 * t + 1] += w * bf16_bits_to_f32(u[t] >> 16);
     }
   };
   const u16 *src = cache_o + rh * D + 8 * c;
 #pragma unroll
   for (int p = 0; p < PMAX; ++p)
-    if (p < P) add(src + p * plane_o, lv[p]);
-  if (sel.has_extra) add(extra_o + rh * D + 8 * c, lv[PMAX]);
+    if (p < P && ((pm >> p) & 1)) add(src + p * plane_o, wts[p]);
+  if (sel.has_extra) add(extra_o + rh * D + 8 * c, wts[PMAX]);
   uint4 res;
   res.x = pack_bf16x2(acc[0], acc[1]);
   res.y = pack_bf16x2(acc[2], acc[3]);
