@@ -211,8 +211,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=64, help="oracle sample rows per query block")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the path shards by query block across GPUs, which is not built here)"}))
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1 "
+                                   "(the path would shard by query block across GPUs; that exchange is not implemented)"}))
         return 2
 
     import torch

@@ -71,7 +71,7 @@ typedef enum {
   DIT_ERR_MASK = -4,          /* recompute value not 0/1, local partition not recomputed, bad local_part */
   DIT_ERR_CACHE_INVALID = -5, /* reuse (or delta) of a cache slot that cache_valid marks never computed */
   DIT_ERR_WORKSPACE = -6,     /* workspace NULL or smaller than dit_attn_workspace_bytes() */
-  DIT_ERR_UNSUPPORTED = -7,   /* D not in {64, 128}, or a mode this build does not implement */
+  DIT_ERR_UNSUPPORTED = -7,   /* D not in {64, 128}, or a mode the library does not implement */
   DIT_ERR_HIP = -8,           /* a HIP launch failed */
   DIT_ERR_INTERNAL = -9       /* unexpected internal error */
 } dit_status;
