@@ -189,3 +189,41 @@ def test_fp8_rejects_invalid_and_unsupported():
     with pytest.raises(api.DitError):
         api.partition_attention_fp8(q, PT.to_dev(X.k), PT.to_dev(X.v), w.q_offsets, w.kv_offsets,
                                     np.ones((w.n_qb, w.P), np.uint8), g.sa.cache_o, None, g.sa.cache_lse)
+
+
+def test_fp8_longvideo_trajectory_reduced_grid():
+    """10 denoising steps with the compressed cache: anchor every 5, groups of 4, the w*delta
+    planner fed by the GPU's own importance and fp8 delta.  Every step's output stays within
+    the e4m3 rounding bound of the oracle's exact step under the same masks, and the anchor
+    steps' importance (from lse, which is not compressed) matches the oracle's."""
+    w = W.workload("longvideo", grid=(9, 18, 32), H=2)
+    rows = np.arange(w.S_q)
+    g = Fp8Run(w)
+    o = PT.OracleRun(w, rows)
+    cp = api.Planner(w.n_qb, w.P, w.group_offsets, w.local_part, w.anchor_every, w.recompute_groups, "wdelta")
+    worst = 0.0
+    for t in range(w.steps):
+        X = W.make_step(w, t)
+        mask, _ = cp.next(t)
+        anchor = t % w.anchor_every == 0
+        did = g.step(X, mask, want_importance=anchor, want_delta=t > 0)
+        res = o.step(X, mask)
+        s_exact = np.abs(o.cache.exact_O).max(axis=-1) / 448.0
+        qb = np.maximum(np.abs(o.cache.exact_O) * 2.0 ** -4, s_exact[..., None] * 2.0 ** -10)
+        Wt = np.transpose(res.weights, (0, 2, 1))[:, :, :, None]
+        bound = (Wt * qb).sum(axis=0) * (1 + 2.0 ** -4) + PT.O_ABS_TOL
+        err = np.abs(g.out_rows(rows) - res.O)
+        worst = max(worst, float((err / bound).max()))
+        _log(f"step {t} anchor={anchor} recomputed={int(mask.sum())} max|dO|={err.max():.3e} "
+             f"bound ratio {(err / bound).max():.3f}")
+        assert (err <= bound).all(), t
+        imp = None
+        if anchor:
+            imp = g.sa.importance[0].cpu().numpy()
+            assert np.abs(imp - oracle.importance(res.weights, rows, w.q_offsets)).max() <= PT.IMP_ABS_TOL
+        d = g.sa.delta[0].cpu().numpy() if did else None
+        if d is not None:
+            assert np.isfinite(d).all() and (d > 0).all()
+        cp.observe(t, imp, d)
+    cp.close()
+    _log("worst bound ratio over the trajectory", worst)
