@@ -56,9 +56,18 @@ def cpu_baseline(w: W.Workload, X: "W.StepInputs", mask: np.ndarray, rows_per_bl
     """Time the oracle's step work (recomputed partition states + merge) on a row sample."""
     import oracle
     try:
-        threads = len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except AttributeError:
-        threads = os.cpu_count() or 1
+        affinity = os.cpu_count() or 1
+    # the oracle's parallel work is its BLAS matrix products: report that pool's thread count
+    threads = affinity
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [d["num_threads"] for d in threadpool_info() if d.get("user_api") == "blas"]
+        if blas:
+            threads = min(max(blas), affinity)
+    except Exception:
+        pass
     rows = np.concatenate([np.arange(w.q_offsets[i], w.q_offsets[i] + min(rows_per_block, w.q_offsets[i + 1] - w.q_offsets[i]))
                            for i in range(w.n_qb)])
     q = W.to_f64(X.q[0][rows])
@@ -76,7 +85,8 @@ def cpu_baseline(w: W.Workload, X: "W.StepInputs", mask: np.ndarray, rows_per_bl
     dt = time.perf_counter() - t0
     blk = oracle.block_of_rows(rows, w.q_offsets)
     flop = float(4 * w.D * w.H * sum(int(mask[b].astype(np.int64) @ sizes) for b in blk))
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "host_cpus_available": affinity,
+            "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"{len(rows)} of {w.S_q} query rows (first {rows_per_block} of each of the {w.n_qb} "
                       f"query blocks), all {w.H} heads: fp64 states of the recomputed partitions and the "
