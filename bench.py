@@ -99,6 +99,19 @@ def kernel_source_sha256() -> str:
     return hashlib.sha256(b"".join(open(os.path.join(d, f), "rb").read() for f in ("kernels.hip", "launch.h"))).hexdigest()
 
 
+def measured_counters(workload: str) -> dict:
+    """Counter-derived figures of the attention kernel (clock under load, MFMA busy fraction)
+    from the committed rocprofv3 summary of this workload; empty when the kernel sources
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return {}
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != kernel_source_sha256():
+        return {}
+    return rec.get("attention_counters", {})
+
+
 def measured_traffic(workload: str) -> dict:
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this
     workload, scaled by the copy-kernel calibration; empty when the kernel sources changed since
@@ -425,7 +438,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic,
                      "kernel": "partition_attention_kernel<128, false>", "ms": round(attn_ms, 4),
-                     "algorithmic_flop": flop},
+                     "algorithmic_flop": flop, "counters": measured_counters(w.name) or None},
         "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4), "traffic": merge_traffic,
                            "kernel": "state_merge_kernel<128,16>", "ms": round(merge_ms, 4),

@@ -25,3 +25,18 @@ def test_traffic_record_matches_kernel_sources_or_is_ignored():
         assert got and all(v > 0 for v in got.values())
     else:
         assert got == {}
+
+
+def test_counter_record_follows_the_same_source_hash():
+    """The attention kernel's counter figures are reported under the same hash guard, and are
+    self-consistent: the clock-scaled peak follows from the nominal peak at 2.4 GHz."""
+    sys.path.insert(0, ROOT)
+    import bench
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_video720p.json")))
+    got = bench.measured_counters("video720p")
+    if rec["source_sha256"] != bench.kernel_source_sha256():
+        assert got == {}
+        return
+    assert 0.5 < got["clock_ghz_under_load"] <= 2.4
+    assert 0.0 < got["mfma_busy_frac"] <= 1.0
+    assert abs(got["peak_tflops_at_that_clock"] - 2500.0 * got["clock_ghz_under_load"] / 2.4) < 1.0
