@@ -306,6 +306,8 @@ def main() -> int:
     flop = attn_flop(w, mask)
     mbytes = merge_bytes(w)
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
+    # clock under load and MFMA busy fraction from the committed counter record (None when stale)
+    attn_counters = measured_counters(w.name)
     merge_gbs = mbytes / (merge_ms * 1e-3) / 1e9
     log(f"[bench] step {ms_step:.3f} ms  attention {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s)  "
         f"merge {merge_ms:.3f} ms ({merge_gbs:.0f} GB/s)  finalize {fin_ms:.4f} ms")
@@ -438,7 +440,9 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic,
                      "kernel": "partition_attention_kernel<128, false>", "ms": round(attn_ms, 4),
-                     "algorithmic_flop": flop, "counters": measured_counters(w.name) or None},
+                     "algorithmic_flop": flop, "counters": attn_counters or None,
+                     "frac_of_clock_peak": (round(attn_tflops / attn_counters["peak_tflops_at_that_clock"], 4)
+                                            if attn_counters else None)},
         "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4), "traffic": merge_traffic,
                            "kernel": "state_merge_kernel<128,16>", "ms": round(merge_ms, 4),
