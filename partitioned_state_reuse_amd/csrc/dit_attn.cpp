@@ -20,6 +20,9 @@ int check_dims(int B, int S_q, int S_kv, int H, int D) {
   // element offsets are 64-bit in the kernels; grid sizes and row indices are 32-bit
   if ((int64_t)S_q * H > (int64_t)1 << 31 || (int64_t)S_kv * H > (int64_t)1 << 31)
     return DIT_ERR_SHAPE;
+  // a dispatch counts its work-items in 32 bits: the merge kernels run D / 8 threads per
+  // row-head of all B batches
+  if ((int64_t)B * S_q * H * (D / 8) > (int64_t)UINT32_MAX) return DIT_ERR_SHAPE;
   return DIT_OK;
 }
 
@@ -115,7 +118,9 @@ int build_attn(const void *q, const void *k, const void *v, int B, int S_q, int 
     desc.item_prefix[p + 1] = desc.item_prefix[p] + items;
   }
   desc.items_per_head = desc.item_prefix[P];
-  if ((int64_t)B * H * desc.items_per_head > INT32_MAX) return DIT_ERR_SHAPE;
+  // one workgroup of kWaves * 64 threads per (batch, head, item); a dispatch counts its
+  // work-items in 32 bits
+  if ((int64_t)B * H * desc.items_per_head * (dit::kWaves * 64) > (int64_t)UINT32_MAX) return DIT_ERR_SHAPE;
   for (int i = 0; i < n_qb; ++i) desc.local_part[i] = (want_delta && local_part) ? local_part[i] : -1;
   return DIT_OK;
 }

@@ -78,6 +78,12 @@ def test_validation_rejects_before_launch(L, kw, code):
     assert _call(L, **kw) == code
 
 
+def test_attention_grid_beyond_32_bit_work_items(L):
+    """2M query rows, 40 heads, 64 recomputed partitions: 1e6 items per head x 256 threads."""
+    S_q = 2_000_000
+    assert _call(L, S_q=S_q, S_kv=64, H=40, D=128, qo=(0, S_q), ko=tuple(range(65)), rec=(1,) * 64) == -2
+
+
 def test_too_many_blocks_or_partitions(L):
     qo = list(range(0, 66))
     assert _call(L, S_q=65, qo=qo, rec=[1, 0] * 65, local=[0] * 65) == -2
@@ -110,6 +116,8 @@ def _u8(s):
     # dit_state_merge(o, lse, B, S_q, H, D, P, out, lse_out, st)
     (lambda L: L.dit_state_merge(1, 1, 1, 8, 1, 64, 0, 1, 1, None), -2),
     (lambda L: L.dit_state_merge(1, None, 1, 8, 1, 64, 2, 1, 1, None), -1),
+    # 8M rows x 40 heads x 16 threads per row-head: more work-items than one dispatch can count
+    (lambda L: L.dit_state_merge(1, 1, 1, 8_000_000, 40, 128, 2, 1, 1, None), -2),
     # dit_state_merge_masked(o, lse, B, S_q, H, D, P, qo, n_qb, sel, extra_o, extra_lse, out, lse_out, st)
     (lambda L: L.dit_state_merge_masked(1, 1, 1, 8, 1, 64, 2, _i32([0, 8]), 1, _u8([1, 2]), None, None, 1, 1, None), -4),
     (lambda L: L.dit_state_merge_masked(1, 1, 1, 8, 1, 64, 2, _i32([0, 9]), 1, _u8([1, 0]), None, None, 1, 1, None), -3),
