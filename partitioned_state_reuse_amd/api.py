@@ -42,10 +42,6 @@ def _u8(arr) -> ctypes.Array:
     return (ctypes.c_uint8 * len(a)).from_buffer_copy(a.tobytes())
 
 
-def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
-
-
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -60,10 +56,39 @@ def _dims(q: torch.Tensor, k: torch.Tensor) -> Tuple[int, int, int, int, int]:
     return B, S_q, S_kv, H, D
 
 
-def _require(t: torch.Tensor, dtype, shape, name: str) -> None:
-    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name}: need contiguous {dtype} cuda tensor of shape {tuple(shape)}, "
-                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+def _dev(t: Optional[torch.Tensor], dtype, shape, name: str) -> Optional[int]:
+    """Device address of `t` once it is known to be a contiguous GPU tensor of the expected
+    dtype and shape (`shape` None: any).  The library reads every pointer as raw device
+    memory of the documented layout, so a host tensor or a strided view must not reach it.
+    None passes through (the library reports a missing required pointer itself)."""
+    if t is None:
+        return None
+    if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype or not t.is_contiguous()
+            or (shape is not None and tuple(t.shape) != tuple(shape))):
+        got = (f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}"
+               if isinstance(t, torch.Tensor) else type(t).__name__)
+        want = "any shape" if shape is None else f"shape {tuple(shape)}"
+        raise ValueError(f"{name}: need a contiguous {dtype} GPU tensor of {want}, got {got}")
+    return t.data_ptr()
+
+
+BF16, F32, U8 = torch.bfloat16, torch.float32, torch.uint8
+
+
+def _qkv(q, k, v):
+    """Shapes of q [B,S_q,H,D] and k, v [B,S_kv,H,D] and their device addresses."""
+    if q is None or k is None:
+        raise ValueError("q and k are required")
+    B, S_q, S_kv, H, D = _dims(q, k)
+    return (B, S_q, S_kv, H, D), (_dev(q, BF16, (B, S_q, H, D), "q"), _dev(k, BF16, (B, S_kv, H, D), "k"),
+                                  _dev(v, BF16, (B, S_kv, H, D), "v"))
+
+
+def _ws(t: Optional[torch.Tensor], name: str) -> Tuple[Optional[int], int]:
+    """Address and byte size of a float32 workspace (any shape)."""
+    if t is None:
+        return None, 0
+    return _dev(t, F32, None, name), t.numel() * t.element_size()
 
 
 def workspace_bytes(B: int, S_q: int, H: int, D: int, n_qb: int, P: int) -> int:
@@ -76,81 +101,96 @@ def attn_partitioned(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_l
     """One selective step: dit_attn_partitioned.  Tensors are device tensors in the
     layouts of include/dit_attn.h; offsets, mask, local_part and cache_valid are host
     sequences/arrays."""
-    B, S_q, S_kv, H, D = _dims(q, k)
+    (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
     n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wp, ws_bytes = _ws(workspace, "workspace")
     _check(_lib.lib().dit_attn_partitioned(
-        _ptr(q), _ptr(k), _ptr(v), B, S_q, S_kv, H, D,
+        qp, kp, vp, B, S_q, S_kv, H, D,
         _i32(q_offsets), n_qb, _i32(kv_offsets), P,
         None if local_part is None else _i32(local_part), _u8(recompute),
         None if cache_valid is None else _u8(cache_valid),
-        _ptr(cache_o), _ptr(cache_lse), _ptr(out), _ptr(lse), float(scale),
-        _ptr(importance_out), _ptr(delta_out), _ptr(workspace), ws_bytes, _stream(stream)))
+        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"),
+        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), float(scale),
+        _dev(importance_out, F32, (B, n_qb, P), "importance_out"), _dev(delta_out, F32, (B, n_qb), "delta_out"),
+        wp, ws_bytes, _stream(stream)))
 
 
 def partition_attention(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, *,
                         local_part=None, scale: float = 0.0, delta_partials=None, stream=None) -> None:
-    B, S_q, S_kv, H, D = _dims(q, k)
+    (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
     n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
-    ws_bytes = 0 if delta_partials is None else delta_partials.numel() * delta_partials.element_size()
+    wp, ws_bytes = _ws(delta_partials, "delta_partials")
     _check(_lib.lib().dit_partition_attention(
-        _ptr(q), _ptr(k), _ptr(v), B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
-        None if local_part is None else _i32(local_part), _u8(recompute), _ptr(cache_o), _ptr(cache_lse),
-        float(scale), _ptr(delta_partials), ws_bytes, _stream(stream)))
+        qp, kp, vp, B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
+        None if local_part is None else _i32(local_part), _u8(recompute),
+        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"),
+        float(scale), wp, ws_bytes, _stream(stream)))
 
 
 def partition_attention_fp8(q, k, v, q_offsets, kv_offsets, recompute, cache_q8, cache_scale, cache_lse, *,
                             local_part=None, scale: float = 0.0, delta_partials=None, stream=None) -> None:
     """partition_attention into the compressed cache (cache_q8 uint8 e4m3 codes,
     cache_scale one f32 scale per partition, batch, head and row)."""
-    B, S_q, S_kv, H, D = _dims(q, k)
+    (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
     n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
-    ws_bytes = 0 if delta_partials is None else delta_partials.numel() * delta_partials.element_size()
+    wp, ws_bytes = _ws(delta_partials, "delta_partials")
     _check(_lib.lib().dit_partition_attention_fp8(
-        _ptr(q), _ptr(k), _ptr(v), B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
-        None if local_part is None else _i32(local_part), _u8(recompute), _ptr(cache_q8), _ptr(cache_scale),
-        _ptr(cache_lse), float(scale), _ptr(delta_partials), ws_bytes, _stream(stream)))
+        qp, kp, vp, B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
+        None if local_part is None else _i32(local_part), _u8(recompute),
+        _dev(cache_q8, U8, (P, B, S_q, H, D), "cache_q8"), _dev(cache_scale, F32, (P, B, H, S_q), "cache_scale"),
+        _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), float(scale), wp, ws_bytes, _stream(stream)))
 
 
 def state_merge_fp8(cache_q8, cache_scale, cache_lse, out, lse, *, stream=None) -> None:
     P, B, S_q, H, D = cache_q8.shape
-    _check(_lib.lib().dit_state_merge_fp8(_ptr(cache_q8), _ptr(cache_scale), _ptr(cache_lse), B, S_q, H, D, P,
-                                          _ptr(out), _ptr(lse), _stream(stream)))
+    _check(_lib.lib().dit_state_merge_fp8(
+        _dev(cache_q8, U8, None, "cache_q8"), _dev(cache_scale, F32, (P, B, H, S_q), "cache_scale"),
+        _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), B, S_q, H, D, P,
+        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), _stream(stream)))
 
 
 def state_merge(cache_o, cache_lse, out, lse, *, stream=None) -> None:
     P, B, S_q, H, D = cache_o.shape
-    _check(_lib.lib().dit_state_merge(_ptr(cache_o), _ptr(cache_lse), B, S_q, H, D, P, _ptr(out), _ptr(lse),
-                                      _stream(stream)))
+    _check(_lib.lib().dit_state_merge(
+        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), B, S_q, H, D, P,
+        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), _stream(stream)))
 
 
 def state_merge_masked(cache_o, cache_lse, q_offsets, plane_select, out, lse, *, extra_o=None, extra_lse=None,
                        stream=None) -> None:
     """Merge, per query block, only the selected cache planes (plus an optional extra state)."""
     P, B, S_q, H, D = cache_o.shape
-    _check(_lib.lib().dit_state_merge_masked(_ptr(cache_o), _ptr(cache_lse), B, S_q, H, D, P, _i32(q_offsets),
-                                             len(q_offsets) - 1, _u8(plane_select), _ptr(extra_o), _ptr(extra_lse),
-                                             _ptr(out), _ptr(lse), _stream(stream)))
+    _check(_lib.lib().dit_state_merge_masked(
+        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), B, S_q, H, D, P,
+        _i32(q_offsets), len(q_offsets) - 1, _u8(plane_select),
+        _dev(extra_o, BF16, (B, S_q, H, D), "extra_o"), _dev(extra_lse, F32, (B, H, S_q), "extra_lse"),
+        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), _stream(stream)))
 
 
 def state_compose(cache_o, cache_lse, group_offsets, out_o, out_lse, *, stream=None) -> None:
     """Compose runs of adjacent cached partition states into coarser group states."""
     P, B, S_q, H, D = cache_o.shape
-    _check(_lib.lib().dit_state_compose(_ptr(cache_o), _ptr(cache_lse), P, _i32(group_offsets),
-                                        len(group_offsets) - 1, B, S_q, H, D, _ptr(out_o), _ptr(out_lse),
-                                        _stream(stream)))
+    G = len(group_offsets) - 1
+    _check(_lib.lib().dit_state_compose(
+        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), P,
+        _i32(group_offsets), G, B, S_q, H, D,
+        _dev(out_o, BF16, (G, B, S_q, H, D), "out_o"), _dev(out_lse, F32, (G, B, H, S_q), "out_lse"),
+        _stream(stream)))
 
 
 def importance(cache_lse, lse, q_offsets, importance_out, *, stream=None) -> None:
     P, B, H, S_q = cache_lse.shape
-    _check(_lib.lib().dit_importance(_ptr(cache_lse), _ptr(lse), B, S_q, H, P, _i32(q_offsets),
-                                     len(q_offsets) - 1, _ptr(importance_out), _stream(stream)))
+    n_qb = len(q_offsets) - 1
+    _check(_lib.lib().dit_importance(
+        _dev(cache_lse, F32, None, "cache_lse"), _dev(lse, F32, (B, H, S_q), "lse"), B, S_q, H, P,
+        _i32(q_offsets), n_qb, _dev(importance_out, F32, (B, n_qb, P), "importance_out"), _stream(stream)))
 
 
 def local_change_finalize(delta_partials, B, S_q, H, D, q_offsets, delta_out, *, stream=None) -> None:
-    ws_bytes = delta_partials.numel() * delta_partials.element_size()
-    _check(_lib.lib().dit_local_change_finalize(_ptr(delta_partials), ws_bytes, B, S_q, H, D, _i32(q_offsets),
-                                                len(q_offsets) - 1, _ptr(delta_out), _stream(stream)))
+    wp, ws_bytes = _ws(delta_partials, "delta_partials")
+    n_qb = len(q_offsets) - 1
+    _check(_lib.lib().dit_local_change_finalize(wp, ws_bytes, B, S_q, H, D, _i32(q_offsets), n_qb,
+                                                _dev(delta_out, F32, (B, n_qb), "delta_out"), _stream(stream)))
 
 
 class Planner:

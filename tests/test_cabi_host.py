@@ -78,6 +78,25 @@ def test_validation_rejects_before_launch(L, kw, code):
     assert _call(L, **kw) == code
 
 
+def test_binding_refuses_host_and_mismatched_tensors(L):
+    """The Python binding hands the library raw device addresses, so it checks device,
+    dtype, contiguity and shape first (a host tensor here would be read as device memory)."""
+    import torch
+    from partitioned_state_reuse_amd import api
+    co = torch.zeros((2, 1, 8, 1, 64), dtype=torch.bfloat16)
+    cl = torch.zeros((2, 1, 1, 8))
+    out = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)
+    lse = torch.zeros((1, 1, 8))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.state_merge(co, cl, out, lse)
+    q = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.partition_attention(q, q, q, [0, 8], [0, 4, 8], [[1, 1]], co, cl)
+    with pytest.raises(ValueError, match="disagree"):
+        api.partition_attention(q, torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16), q, [0, 8], [0, 4, 8],
+                                [[1, 1]], co, cl)
+
+
 def test_attention_grid_beyond_32_bit_work_items(L):
     """2M query rows, 40 heads, 64 recomputed partitions: 1e6 items per head x 256 threads."""
     S_q = 2_000_000

@@ -59,9 +59,10 @@ def test_group_compose_then_continue_at_group_level():
 
 def test_compose_rejects_bad_offsets():
     sa = api.SelectiveAttention(1, 64, 64, 1, 64, [0, 64], [0, 16, 32, 48, 64], [0])
-    out_o = torch.empty((2, 1, 64, 1, 64), dtype=torch.bfloat16, device="cuda")
-    out_l = torch.empty((2, 1, 1, 64), dtype=torch.float32, device="cuda")
     for bad in ([0, 2, 3], [0, 2, 2, 4], [1, 4]):
+        G = len(bad) - 1    # output buffers sized for the groups the offsets claim
+        out_o = torch.empty((G, 1, 64, 1, 64), dtype=torch.bfloat16, device="cuda")
+        out_l = torch.empty((G, 1, 1, 64), dtype=torch.float32, device="cuda")
         with pytest.raises(api.DitError):
             api.state_compose(sa.cache_o, sa.cache_lse, bad, out_o, out_l)
 
