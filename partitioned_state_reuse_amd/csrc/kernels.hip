@@ -842,9 +842,39 @@ __global__ __launch_bounds__(256) void state_merge_masked_kernel(
     }
   };
   const u16 *src = cache_o + rh * D + 8 * c;
+  // the selected planes in increasing order, NB loads in flight at a time; a short last
+  // batch re-reads its first plane in place of the missing ones (never added)
+  constexpr int NB = PMAX < kMaskedMergeBatch ? PMAX : kMaskedMergeBatch;
+  uint64_t rest = pm & (P < 64 ? ((uint64_t)1 << P) - 1 : ~(uint64_t)0);
+  while (rest) {
+    int pi[NB];
+    pi[0] = __builtin_ctzll(rest);
+    rest &= rest - 1;
+    int n = 1;
 #pragma unroll
-  for (int p = 0; p < PMAX; ++p)
-    if (p < P && ((pm >> p) & 1)) add(src + p * plane_o, wts[p]);
+    for (int j = 1; j < NB; ++j) {
+      pi[j] = pi[0];
+      if (rest) {
+        pi[j] = __builtin_ctzll(rest);
+        rest &= rest - 1;
+        n = j + 1;
+      }
+    }
+    u32x4 u[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) u[j] = __builtin_nontemporal_load((const u32x4 *)(src + (int64_t)pi[j] * plane_o));
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j < n) {
+        const float w = wts[pi[j]];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[2 * t] += w * bf16_bits_to_f32(u[j][t] & 0xffffu);
+          acc[2 * t + 1] += w * bf16_bits_to_f32(u[j][t] >> 16);
+        }
+      }
+    }
+  }
   if (sel.has_extra) add(extra_o + rh * D + 8 * c, wts[PMAX]);
   uint4 res;
   res.x = pack_bf16x2(acc[0], acc[1]);

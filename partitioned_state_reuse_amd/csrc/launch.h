@@ -35,6 +35,11 @@ constexpr bool kSetPrio = DIT_ATTN_SETPRIO != 0;
 #endif
 // query rows (of all heads) whose merge workgroups run on one XCD in a row (0: round-robin)
 constexpr int kMergeChunkRows = DIT_MERGE_CHUNK_ROWS;
+#ifndef DIT_MERGE_MASKED_BATCH
+#define DIT_MERGE_MASKED_BATCH 4
+#endif
+// selected cache planes whose loads a masked-merge thread keeps in flight together
+constexpr int kMaskedMergeBatch = DIT_MERGE_MASKED_BATCH;
 #ifndef DIT_MERGE_FP8_DPT
 #define DIT_MERGE_FP8_DPT 16
 #endif
