@@ -295,12 +295,29 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+    if constexpr (MB == 1) {
+      // operands read kReadAhead MFMAs ahead; the scheduling barriers keep that distance
+      bf16x8 ka[KK];
+      auto kread = [&](int kk) {
+        ka[kk] = as_bf16x8(*(const uint4 *)((const char *)Kt + (k_lane ^ (uint32_t)(kk << 5))));
+      };
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+      for (int kk = 0; kk < kReadAhead && kk < KK; ++kk) kread(kk);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 a = as_bf16x8(*(const uint4 *)((const char *)Kt + (k_lane ^ (uint32_t)(kk << 5)) + mb * 64 * D));
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + kReadAhead < KK) kread(kk + kReadAhead);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s[0], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const bf16x8 a = as_bf16x8(*(const uint4 *)((const char *)Kt + (k_lane ^ (uint32_t)(kk << 5)) + mb * 64 * D));
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
+        }
       }
     }
   };
@@ -362,19 +379,28 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   };
   // O^T += V^T P^T over the 16-key steps.  k-index 8 hh + j of step c stands for key
   // 16 c + 4 hh + 8 (j >> 2) + (j & 3) on both operands.
+  // MFMA i of the tile takes step c = i / DB and d-block db = i % DB; its V^T operand is
+  // read kReadAhead MFMAs ahead.
   auto pv = [&](const u16 *Vt, const bf16x8 (&pb)[NC]) {
+    constexpr int NPV = NC * DB;
+    bf16x8 va[NPV];
+    auto vread = [&](int i) {
+      const int c = i / DB, db = i % DB;
+      const u16 *vp = (const u16 *)((const char *)Vt + (v_lane ^ (uint32_t)(db << 6)) + 32 * c * D);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds *)(vp));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds *)(vp + 8 * D));
+      const uint2 lo2 = __builtin_bit_cast(uint2, lo);
+      const uint2 hi2 = __builtin_bit_cast(uint2, hi);
+      va[i] = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+    };
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int i = 0; i < kReadAhead && i < NPV; ++i) vread(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u16 *vp = (const u16 *)((const char *)Vt + (v_lane ^ (uint32_t)(db << 6)) + 32 * c * D);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds *)(vp));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_lds *)(vp + 8 * D));
-        const uint2 lo2 = __builtin_bit_cast(uint2, lo);
-        const uint2 hi2 = __builtin_bit_cast(uint2, hi);
-        const bf16x8 a = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], o[db], 0, 0, 0);
-      }
+    for (int i = 0; i < NPV; ++i) {
+      if (i + kReadAhead < NPV) vread(i + kReadAhead);
+      o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[i / DB], o[i % DB], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Wait until this wave's copy of the oldest tile still in flight has landed (the loads of

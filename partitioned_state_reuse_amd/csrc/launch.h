@@ -25,6 +25,11 @@ constexpr int kWaves = DIT_ATTN_WAVES;      // waves per attention workgroup
 constexpr int kBlockM = 32 * kWaves;        // query rows per attention workgroup (32 per wave)
 constexpr int kBlockN = DIT_ATTN_BLOCK_N;   // keys per staged KV tile (32 or 64)
 constexpr int kStages = DIT_ATTN_STAGES;    // K/V tile buffers in the LDS ring (2 or 3)
+#ifndef DIT_ATTN_READ_AHEAD
+#define DIT_ATTN_READ_AHEAD 3
+#endif
+// MFMAs by which the LDS operand reads run ahead of their use in the attention kernel
+constexpr int kReadAhead = DIT_ATTN_READ_AHEAD;
 #ifndef DIT_ATTN_SETPRIO
 #define DIT_ATTN_SETPRIO 0
 #endif
