@@ -65,12 +65,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // Online softmax in base 2, fp32 state, with a lazy running maximum: the maximum used
 // for the exponentials is raised only when a tile's maximum exceeds it by more than
 // kRescaleLog2 (then exponentials stay <= 2^kRescaleLog2 and nothing overflows), which
-// skips the rescale of the accumulators on almost every tile.  P is rounded to bf16 for
+// skips the rescale of the accumulators on almost every tile; the tile's maximum itself is
+// only computed when some lane's sum of the tile's exponentials (taken against the current
+// maximum) exceeds that bound.  P is rounded to bf16 for
 // the product.  The epilogue writes the partition's state into its cache slot (bf16, or
 // e4m3 codes plus a per-row scale with FP8) through an LDS staging buffer and, for a
 // block's local partition, the partial sums of the local-change norm.
 // ------------------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kProbSumBound = 256.0f;  // 2^kRescaleLog2
 
 template <int D>
 struct TileGeom {
@@ -355,10 +358,11 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
   };
-  // Probabilities of a tile, summed into lsum and packed to bf16 as the B operand of the
-  // 16-key PV steps.
+  // Probabilities of a tile against the current running maximum, packed to bf16 as the B
+  // operand of the 16-key PV steps; returns this lane's sum of them (not yet in lsum).
   auto probs = [&](const f32x16 (&s)[MB], bf16x8 (&pb)[NC]) {
     const float negm = -m;
+    float ts = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int mb = c >> 1;
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][base + j], scale_log2, negm));
-        lsum += e[j];
+        ts += e[j];
       }
       uint4 pu;
       pu.x = pack_bf16x2(e[0], e[1]);
@@ -376,6 +380,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       pu.w = pack_bf16x2(e[6], e[7]);
       pb[c] = as_bf16x8(pu);
     }
+    return ts;
   };
   // O^T += V^T P^T over the 16-key steps.  k-index 8 hh + j of step c stands for key
   // 16 c + 4 hh + 8 (j >> 2) + (j & 3) on both operands.
@@ -438,9 +443,18 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       qk(kbuf(st), s);
       if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(0);
       if (kt == ntiles - 1 && last_valid < kBlockN) mask_tail(s, last_valid);
-      rescale(tile_max(s));
+      // Exponentials first, against the running maximum as it stands.  Every probability
+      // is at most the lane's tile sum, so a sum within 2^kRescaleLog2 on every lane keeps
+      // the lazy-maximum bound without computing the tile's maximum.  Otherwise (a sum
+      // above the bound, or not finite, as on the first tile) the maximum is checked, the
+      // accumulators are rescaled if it moved past the bound, and the tile is redone.
       bf16x8 pb[NC];
-      probs(s, pb);
+      float ts = probs(s, pb);
+      if (__ballot(!(ts <= kProbSumBound))) {
+        rescale(tile_max(s));
+        ts = probs(s, pb);
+      }
+      lsum += ts;
       if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);
       pv(vbuf(st), pb);
       if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(0);
