@@ -267,3 +267,32 @@ def test_split_entry_points_match_one_call():
     assert torch.equal(out, a.out) and torch.equal(lse, a.lse)
     assert torch.equal(co, a.cache_o) and torch.equal(cl, a.cache_lse)
     assert torch.equal(imp, a.importance) and torch.equal(dl, a.delta)
+
+
+def test_tile_sum_bound_and_maximum_jumps():
+    """The kernel takes each tile's exponentials against the running maximum first and
+    computes the tile maximum only when a lane's tile sum exceeds 2^8.  Three cases in one
+    sequence of 20 key tiles: the first tile (no maximum yet), a tile whose 32 scores all sit
+    6.5 (base 2) above the running maximum (sum far above 2^8 with no single exponential
+    above it: no rescale), and two keys 29 (base 2) above it (a real rescale).  Scores are
+    built from one direction u: q = 4u + noise, k = a u (+ noise elsewhere)."""
+    rng = np.random.default_rng(11)
+    S, H, D = 640, 2, 128
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q = 4.0 * u + 0.1 * rng.standard_normal((S, H, D))
+    k = 0.1 * rng.standard_normal((S, H, D))
+    v = rng.standard_normal((S, H, D))
+    sq = math.sqrt(D)
+    k[160:192] = (4.5 * sq / 4.0) * u          # tile 5: every score ~ 4.5 (natural log units)
+    k[400:402] = (20.0 * sq / 4.0) * u         # tile 12: two scores ~ 20
+    bits = [W.f32_to_bf16_bits(x[None].astype(np.float32)) for x in (q, k, v)]
+    qd, kd, vd = (W.to_f64(b[0]) for b in bits)
+    s_chk = np.einsum("hd,khd->hk", qd[0], kd) / sq
+    assert s_chk[:, 160:192].min() > 4.0 and s_chk[:, 400:402].min() > 19.0   # the planted scores
+    sa = api.SelectiveAttention(1, S, S, H, D, [0, S], [0, S], [0])
+    sa.step(*(PT.to_dev(b) for b in bits), np.ones((1, 1), np.uint8))
+    torch.cuda.synchronize()
+    O, lse = oracle.full_attention(qd, kd, vd, 1.0 / sq)
+    assert np.abs(PT.bf16_to_f64(sa.out[0]) - O).max() <= PT.O_ABS_TOL
+    assert np.abs(sa.lse[0].double().cpu().numpy() - lse).max() <= PT.LSE_ABS_TOL
