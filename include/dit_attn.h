@@ -67,8 +67,9 @@ typedef enum {
   DIT_OK = 0,
   DIT_ERR_NULL = -1,          /* a required pointer is NULL */
   DIT_ERR_SHAPE = -2,         /* B, S_q, S_kv, H, n_qb or P out of range: S_q*H and S_kv*H
-                                 at most 2^31, B*S_q*H*D/8 and (for the attention launch)
-                                 B*H*(recomputed 128-row tiles)*256 below 2^32 */
+                                 at most 2^31, H*D at most 2^25, B*S_q*H*D/8 and (for the
+                                 attention launch) B*H*(recomputed 128-row tiles)*256 below
+                                 2^32 */
   DIT_ERR_OFFSETS = -3,       /* q_offsets / kv_offsets / group offsets malformed */
   DIT_ERR_MASK = -4,          /* recompute value not 0/1, local partition not recomputed, bad local_part */
   DIT_ERR_CACHE_INVALID = -5, /* reuse (or delta) of a cache slot that cache_valid marks never computed */

@@ -23,6 +23,8 @@ int check_dims(int B, int S_q, int S_kv, int H, int D) {
   // a dispatch counts its work-items in 32 bits: the merge kernels run D / 8 threads per
   // row-head of all B batches
   if ((int64_t)B * S_q * H * (D / 8) > (int64_t)UINT32_MAX) return DIT_ERR_SHAPE;
+  // a K/V tile's rows (kBlockN rows of H * D elements) lie in one 31-bit buffer range
+  if ((int64_t)dit::kBlockN * H * D * 2 > (int64_t)INT32_MAX) return DIT_ERR_SHAPE;
   return DIT_OK;
 }
 

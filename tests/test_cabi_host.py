@@ -103,6 +103,11 @@ def test_attention_grid_beyond_32_bit_work_items(L):
     assert _call(L, S_q=S_q, S_kv=64, H=40, D=128, qo=(0, S_q), ko=tuple(range(65)), rec=(1,) * 64) == -2
 
 
+def test_head_width_beyond_a_tile_buffer_range(L):
+    """H*D above 2^25: 32 key rows of a tile would not fit one 31-bit buffer range."""
+    assert _call(L, H=(1 << 25) // 64 + 1, D=64) == -2
+
+
 def test_too_many_blocks_or_partitions(L):
     qo = list(range(0, 66))
     assert _call(L, S_q=65, qo=qo, rec=[1, 0] * 65, local=[0] * 65) == -2
