@@ -67,9 +67,10 @@ typedef enum {
   DIT_OK = 0,
   DIT_ERR_NULL = -1,          /* a required pointer is NULL */
   DIT_ERR_SHAPE = -2,         /* B, S_q, S_kv, H, n_qb or P out of range: S_q*H and S_kv*H
-                                 at most 2^31, H*D at most 2^25, B*S_q*H*D/8 and (for the
-                                 attention launch) B*H*(recomputed 128-row tiles)*256 below
-                                 2^32 */
+                                 at most 2^31, B*S_q*H*D/8 below 2^32; for the attention
+                                 calls also B*H*(recomputed 128-row tiles)*256 below 2^32 and
+                                 (31*H*D + D)*2 at most 2^31 - 1 bytes (the span of one
+                                 32-key K/V tile's rows: H*D up to 34,636,828 at D = 128) */
   DIT_ERR_OFFSETS = -3,       /* q_offsets / kv_offsets / group offsets malformed */
   DIT_ERR_MASK = -4,          /* recompute value not 0/1, local partition not recomputed, bad local_part */
   DIT_ERR_CACHE_INVALID = -5, /* reuse (or delta) of a cache slot that cache_valid marks never computed */
@@ -123,6 +124,11 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v,
  * the state of block i's query rows over partition p's keys and write it into cache slot
  * (p, rows of i); other slots are untouched.  bf16 MFMA products, fp32 accumulation and
  * softmax.  An empty partition writes O = 0, lse = -inf.
+ *   cache_valid        host [n_qb * P] or NULL, as for dit_attn_partitioned: when given, a
+ *                      slot that is neither recomputed nor marked valid is
+ *                      DIT_ERR_CACHE_INVALID (a merge of the cache after this call would
+ *                      read it), and so is a local slot marked invalid when delta_partials
+ *                      is given.
  *   delta_partials     device or NULL.  When given (with local_part), the kernel also writes,
  *                      per (query tile, head) of each block's local partition, the sums
  *                      sum (O_new - O_old)^2 and sum O_old^2 over the tile's rows and D,
@@ -136,6 +142,7 @@ int dit_partition_attention(const void *q, const void *k, const void *v,
                             const int32_t *kv_offsets, int P,
                             const int32_t *local_part,
                             const uint8_t *recompute,
+                            const uint8_t *cache_valid,
                             void *cache_o, float *cache_lse,
                             float softmax_scale,
                             void *delta_partials, size_t workspace_bytes,
@@ -167,7 +174,10 @@ int dit_state_merge(const void *cache_o, const float *cache_lse,
  * delta_partials of dit_partition_attention_fp8 compare the dequantized new and old slot
  * values.  dit_state_merge_fp8 folds each plane's scale into its merge weight,
  * out = sum_p s_p e^{lse_p - lse} e4m3(c_p), accumulated in fp32, written as bf16.
- * Argument checks and errors as for the bf16 calls; cache_scale must be non-NULL.
+ * Argument checks and errors as for the bf16 calls (cache_valid included: reuse of a slot
+ * marked never computed is DIT_ERR_CACHE_INVALID); cache_scale must be non-NULL.
+ * dit_state_merge_fp8 reads every slot: call it only after a dit_partition_attention_fp8
+ * call that was given the validity bitmap and returned DIT_OK.
  */
 int dit_partition_attention_fp8(const void *q, const void *k, const void *v,
                                 int B, int S_q, int S_kv, int H, int D,
@@ -175,6 +185,7 @@ int dit_partition_attention_fp8(const void *q, const void *k, const void *v,
                                 const int32_t *kv_offsets, int P,
                                 const int32_t *local_part,
                                 const uint8_t *recompute,
+                                const uint8_t *cache_valid,
                                 void *cache_q8, float *cache_scale, float *cache_lse,
                                 float softmax_scale,
                                 void *delta_partials, size_t workspace_bytes,

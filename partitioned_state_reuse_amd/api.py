@@ -116,19 +116,22 @@ def attn_partitioned(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_l
 
 
 def partition_attention(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, *,
-                        local_part=None, scale: float = 0.0, delta_partials=None, stream=None) -> None:
+                        local_part=None, cache_valid=None, scale: float = 0.0, delta_partials=None,
+                        stream=None) -> None:
     (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
     n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
     wp, ws_bytes = _ws(delta_partials, "delta_partials")
     _check(_lib.lib().dit_partition_attention(
         qp, kp, vp, B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
         None if local_part is None else _i32(local_part), _u8(recompute),
+        None if cache_valid is None else _u8(cache_valid),
         _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"),
         float(scale), wp, ws_bytes, _stream(stream)))
 
 
 def partition_attention_fp8(q, k, v, q_offsets, kv_offsets, recompute, cache_q8, cache_scale, cache_lse, *,
-                            local_part=None, scale: float = 0.0, delta_partials=None, stream=None) -> None:
+                            local_part=None, cache_valid=None, scale: float = 0.0, delta_partials=None,
+                            stream=None) -> None:
     """partition_attention into the compressed cache (cache_q8 uint8 e4m3 codes,
     cache_scale one f32 scale per partition, batch, head and row)."""
     (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
@@ -137,6 +140,7 @@ def partition_attention_fp8(q, k, v, q_offsets, kv_offsets, recompute, cache_q8,
     _check(_lib.lib().dit_partition_attention_fp8(
         qp, kp, vp, B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
         None if local_part is None else _i32(local_part), _u8(recompute),
+        None if cache_valid is None else _u8(cache_valid),
         _dev(cache_q8, U8, (P, B, S_q, H, D), "cache_q8"), _dev(cache_scale, F32, (P, B, H, S_q), "cache_scale"),
         _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), float(scale), wp, ws_bytes, _stream(stream)))
 
@@ -277,6 +281,8 @@ class SelectiveAttention:
         slots); the current stream then merges the fresh states with the partial."""
         self._bf16_only("step_overlapped")
         recompute = np.asarray(recompute, dtype=np.uint8).reshape(self.n_qb, self.P)
+        # the pre-merge of the reused planes is enqueued before the attention call validates
+        # the mask, so the validity of those planes is checked here first
         if any(not self.valid[i, p] for i in range(self.n_qb) for p in range(self.P) if not recompute[i, p]):
             raise DitError(-5, status_string(-5))
         if not hasattr(self, "partial_o"):
@@ -290,7 +296,7 @@ class SelectiveAttention:
                            self.partial_lse, stream=side_stream)
         do_delta = want_delta and all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
         partition_attention(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
-                            local_part=self.local_part, scale=scale,
+                            local_part=self.local_part, cache_valid=self.valid, scale=scale,
                             delta_partials=self.workspace if do_delta else None, stream=main)
         done = torch.cuda.Event()
         done.record(side_stream)
@@ -337,10 +343,9 @@ class SelectiveAttention:
         local_valid = all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
         do_delta = want_delta and local_valid
         if self.cache_format == "fp8":
-            if any(not self.valid[i, p] for i in range(self.n_qb) for p in range(self.P) if not recompute[i, p]):
-                raise DitError(-5, status_string(-5))
             partition_attention_fp8(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o,
-                                    self.cache_scale, self.cache_lse, local_part=self.local_part, scale=scale,
+                                    self.cache_scale, self.cache_lse, local_part=self.local_part,
+                                    cache_valid=self.valid, scale=scale,
                                     delta_partials=self.workspace if do_delta else None, stream=stream)
             state_merge_fp8(self.cache_o, self.cache_scale, self.cache_lse, self.out, self.lse, stream=stream)
             if want_importance:

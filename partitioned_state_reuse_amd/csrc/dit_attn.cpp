@@ -23,9 +23,14 @@ int check_dims(int B, int S_q, int S_kv, int H, int D) {
   // a dispatch counts its work-items in 32 bits: the merge kernels run D / 8 threads per
   // row-head of all B batches
   if ((int64_t)B * S_q * H * (D / 8) > (int64_t)UINT32_MAX) return DIT_ERR_SHAPE;
-  // a K/V tile's rows (kBlockN rows of H * D elements) lie in one 31-bit buffer range
-  if ((int64_t)dit::kBlockN * H * D * 2 > (int64_t)INT32_MAX) return DIT_ERR_SHAPE;
   return DIT_OK;
+}
+
+// The attention kernel copies a K/V tile through one buffer resource whose range starts at
+// the tile's first row: the bytes it addresses, kBlockN - 1 row strides of H * D bf16 plus
+// one row of D bf16, must stay within a 31-bit range.
+bool tile_fits_buffer_range(int H, int D) {
+  return ((int64_t)(dit::kBlockN - 1) * H * D + D) * 2 <= (int64_t)INT32_MAX;
 }
 
 int check_q_offsets(const int32_t *q_offsets, int n_qb, int S_q) {
@@ -74,6 +79,7 @@ int build_attn(const void *q, const void *k, const void *v, int B, int S_q, int 
   if (S_kv > 0 && (!k || !v)) return DIT_ERR_NULL;  // no keys: k and v may be NULL
   int st = check_dims(B, S_q, S_kv, H, D);
   if (st) return st;
+  if (!tile_fits_buffer_range(H, D)) return DIT_ERR_SHAPE;
   if ((st = check_q_offsets(q_offsets, n_qb, S_q))) return st;
   if ((st = check_kv_offsets(kv_offsets, P, S_kv))) return st;
   for (int e = 0; e < n_qb * P; ++e)
@@ -132,6 +138,38 @@ float scale_log2_of(float softmax_scale, int D) {
   return s * 1.4426950408889634f;
 }
 
+// One selective step (dit_attn_partitioned) on a given workspace.
+int run_partitioned(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H, int D,
+                    const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P, const int32_t *local_part,
+                    const uint8_t *recompute, const uint8_t *cache_valid, void *cache_o, float *cache_lse, void *out,
+                    float *lse, float softmax_scale, float *importance_out, float *delta_out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  try {
+    if (!out || !lse) return DIT_ERR_NULL;
+    AttnDesc desc;
+    const bool want_delta = delta_out != nullptr;
+    int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
+                        cache_valid, cache_o, cache_lse, want_delta, workspace, workspace_bytes, desc);
+    if (st) return st;
+    hipStream_t s = as_stream(stream);
+    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse, want_delta ? (float *)workspace : nullptr,
+                                        desc, scale_log2_of(softmax_scale, D), s) != hipSuccess)
+      return DIT_ERR_HIP;
+    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, s) != hipSuccess)
+      return DIT_ERR_HIP;
+    BlockDesc bd;
+    fill_blocks(bd, q_offsets, n_qb);
+    if (importance_out &&
+        dit::launch_importance(cache_lse, lse, B, S_q, H, P, bd, importance_out, s) != hipSuccess)
+      return DIT_ERR_HIP;
+    if (want_delta && dit::launch_delta_finalize((const float *)workspace, B, H, bd, delta_out, s) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,14 +199,14 @@ size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P) {
 int dit_partition_attention(const void *q, const void *k, const void *v, int B, int S_q, int S_kv,
                             int H, int D, const int32_t *q_offsets, int n_qb,
                             const int32_t *kv_offsets, int P, const int32_t *local_part,
-                            const uint8_t *recompute, void *cache_o, float *cache_lse,
-                            float softmax_scale, void *delta_partials, size_t workspace_bytes,
-                            void *stream) {
+                            const uint8_t *recompute, const uint8_t *cache_valid, void *cache_o,
+                            float *cache_lse, float softmax_scale, void *delta_partials,
+                            size_t workspace_bytes, void *stream) {
   try {
     AttnDesc desc;
     const bool want_delta = delta_partials != nullptr;
     int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part,
-                        recompute, nullptr, cache_o, cache_lse, want_delta, delta_partials,
+                        recompute, cache_valid, cache_o, cache_lse, want_delta, delta_partials,
                         workspace_bytes, desc);
     if (st) return st;
     if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse, (float *)delta_partials, desc,
@@ -182,15 +220,15 @@ int dit_partition_attention(const void *q, const void *k, const void *v, int B, 
 
 int dit_partition_attention_fp8(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H, int D,
                                 const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P,
-                                const int32_t *local_part, const uint8_t *recompute, void *cache_q8,
-                                float *cache_scale, float *cache_lse, float softmax_scale, void *delta_partials,
-                                size_t workspace_bytes, void *stream) {
+                                const int32_t *local_part, const uint8_t *recompute, const uint8_t *cache_valid,
+                                void *cache_q8, float *cache_scale, float *cache_lse, float softmax_scale,
+                                void *delta_partials, size_t workspace_bytes, void *stream) {
   try {
     if (!cache_scale) return DIT_ERR_NULL;
     AttnDesc desc;
     const bool want_delta = delta_partials != nullptr;
-    int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute, nullptr,
-                        cache_q8, cache_lse, want_delta, delta_partials, workspace_bytes, desc);
+    int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
+                        cache_valid, cache_q8, cache_lse, want_delta, delta_partials, workspace_bytes, desc);
     if (st) return st;
     if (dit::launch_partition_attention(D, true, q, k, v, cache_q8, cache_scale, cache_lse, (float *)delta_partials,
                                         desc, scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
@@ -330,30 +368,9 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v, int B, int
                          void *cache_o, float *cache_lse, void *out, float *lse, float softmax_scale,
                          float *importance_out, float *delta_out, void *workspace, size_t workspace_bytes,
                          void *stream) {
-  try {
-    if (!out || !lse) return DIT_ERR_NULL;
-    AttnDesc desc;
-    const bool want_delta = delta_out != nullptr;
-    int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
-                        cache_valid, cache_o, cache_lse, want_delta, workspace, workspace_bytes, desc);
-    if (st) return st;
-    hipStream_t s = as_stream(stream);
-    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse, want_delta ? (float *)workspace : nullptr,
-                                        desc, scale_log2_of(softmax_scale, D), s) != hipSuccess)
-      return DIT_ERR_HIP;
-    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, s) != hipSuccess)
-      return DIT_ERR_HIP;
-    BlockDesc bd;
-    fill_blocks(bd, q_offsets, n_qb);
-    if (importance_out &&
-        dit::launch_importance(cache_lse, lse, B, S_q, H, P, bd, importance_out, s) != hipSuccess)
-      return DIT_ERR_HIP;
-    if (want_delta && dit::launch_delta_finalize((const float *)workspace, B, H, bd, delta_out, s) != hipSuccess)
-      return DIT_ERR_HIP;
-    return DIT_OK;
-  } catch (...) {
-    return DIT_ERR_INTERNAL;
-  }
+  return run_partitioned(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
+                         cache_valid, cache_o, cache_lse, out, lse, softmax_scale, importance_out, delta_out,
+                         workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -225,33 +225,20 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
     constexpr int S = decltype(st)::value;
     if constexpr (S == 0) return v_lds0; else if constexpr (S == 1) return v_lds1; else return v_lds2;
   };
-  auto issue_k = [&](int t, auto par) {
+  // Issue the copies of K and V tile t.  The last tile of a partition whose length is not a
+  // multiple of kBlockN clamps its rows: its offsets overwrite the full-tile ones once, in a
+  // wave-uniform branch (tile t is issued after every earlier tile).
+  auto issue_kv = [&](int t, auto par) {
     if (t == ntiles - 1 && last_valid < kBlockN) {
-      uint32_t off[G::KB_PER_WAVE];
-      dma_offsets<D, false>(rowstride, last_valid, wave_u, lane, off);
-      issue_tile<D>(kbase + t * tile_step, off, kbuf(par), wave_u, tile_bytes);
-    } else {
-      issue_tile<D>(kbase + t * tile_step, koff_full, kbuf(par), wave_u, tile_bytes);
+      dma_offsets<D, false>(rowstride, last_valid, wave_u, lane, koff_full);
+      dma_offsets<D, true>(rowstride, last_valid, wave_u, lane, voff_full);
     }
-  };
-  auto issue_v = [&](int t, auto par) {
-    if (t == ntiles - 1 && last_valid < kBlockN) {
-      uint32_t off[G::KB_PER_WAVE];
-      dma_offsets<D, true>(rowstride, last_valid, wave_u, lane, off);
-      issue_tile<D>(vbase + t * tile_step, off, vbuf(par), wave_u, tile_bytes);
-    } else {
-      issue_tile<D>(vbase + t * tile_step, voff_full, vbuf(par), wave_u, tile_bytes);
-    }
+    issue_tile<D>(kbase + t * tile_step, koff_full, kbuf(par), wave_u, tile_bytes);
+    issue_tile<D>(vbase + t * tile_step, voff_full, vbuf(par), wave_u, tile_bytes);
   };
   // prologue: the first kStages - 1 tiles in flight
-  if (ntiles > 0) {
-    issue_k(0, S0{});
-    issue_v(0, S0{});
-  }
-  if (kStages > 2 && ntiles > 1) {
-    issue_k(1, S1{});
-    issue_v(1, S1{});
-  }
+  if (ntiles > 0) issue_kv(0, S0{});
+  if (kStages > 2 && ntiles > 1) issue_kv(1, S1{});
 
   // ---- this lane's query row, as the B operand: Q[row][16 kk + 8 hh + 0..7]
   const int qrow = wave * 32 + l32;
@@ -346,7 +333,8 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   };
   // Lazy running maximum: raise it (and rescale the accumulators) only when the tile's
   // maximum exceeds it by more than kRescaleLog2 for some lane of the wave.
-  auto rescale = [&](float mt) {
+  // Returns whether the maximum moved (wave-uniform).
+  auto rescale = [&](float mt) -> bool {
     if (__ballot(mt > m + kRescaleLog2)) {
       const float mnew = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -356,13 +344,15 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      return true;
     }
+    return false;
   };
   // Probabilities of a tile against the current running maximum, packed to bf16 as the B
   // operand of the 16-key PV steps; returns this lane's sum of them (not yet in lsum).
   auto probs = [&](const f32x16 (&s)[MB], bf16x8 (&pb)[NC]) {
     const float negm = -m;
-    float ts = 0.f;
+    float ts;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int mb = c >> 1;
@@ -371,7 +361,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][base + j], scale_log2, negm));
-        ts += e[j];
+        ts = (c == 0 && j == 0) ? e[j] : ts + e[j];
       }
       uint4 pu;
       pu.x = pack_bf16x2(e[0], e[1]);
@@ -433,10 +423,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
     constexpr int S = decltype(st)::value;
     using Sa = std::integral_constant<int, (S + kStages - 1) % kStages>;
     const bool ahead = kt + kStages - 1 < ntiles;
-    if (ahead) {
-      issue_k(kt + kStages - 1, Sa{});
-      issue_v(kt + kStages - 1, Sa{});
-    }
+    if (ahead) issue_kv(kt + kStages - 1, Sa{});
     if (active) {
       f32x16 s[MB];
       if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);
@@ -448,11 +435,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       // the lazy-maximum bound without computing the tile's maximum.  Otherwise (a sum
       // above the bound, or not finite, as on the first tile) the maximum is checked, the
       // accumulators are rescaled if it moved past the bound, and the tile is redone.
+      // When no lane's maximum moved past the bound, every exponential already taken is at
+      // most 2^kRescaleLog2 and the tile is kept as it is.
       bf16x8 pb[NC];
       float ts = probs(s, pb);
       if (__ballot(!(ts <= kProbSumBound))) {
-        rescale(tile_max(s));
-        ts = probs(s, pb);
+        if (rescale(tile_max(s))) ts = probs(s, pb);
       }
       lsum += ts;
       if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);

@@ -4,7 +4,14 @@ C ABI binding) and through the fp64 oracle on the same seeded inputs, and compar
 Tolerances (fixed by the target of the path): merged bf16 output max |err| <= 1e-2 and
 lse max |err| <= 1e-3 (fp32 accumulation); in addition the relative Frobenius error of the
 output must stay <= 1e-2, which is the meaningful bound at long sequence lengths where
-|O| itself is far below 1e-2.
+|O| itself is far below 1e-2, and every output element must lie within 2^-6 of its row's
+largest magnitude (row = one query row and head, over D) of the oracle's value.  That bound
+is derived from the arithmetic: the output is rounded to bf16 (half an ulp is 2^-9
+relative), each cached state to bf16 on both sides, where the two roundings can differ by
+one ulp (2^-8 relative) of a state of at most the row's magnitude, and the bf16
+probabilities of the P V product add 2^-9 relative per term; 2^-6 leaves a factor of about
+two over their sum.  Unlike the absolute 1e-2, it scales with |O| and so bites at every
+sequence length: a mis-masked tail or a wrong partition in a few rows fails it.
 """
 from __future__ import annotations
 
@@ -22,6 +29,8 @@ from partitioned_state_reuse_amd import api
 O_ABS_TOL = 1e-2
 LSE_ABS_TOL = 1e-3
 O_REL_FRO_TOL = 1e-2
+O_ROW_REL_TOL = 2.0 ** -6
+O_ROW_ABS_FLOOR = 1e-6
 # importance is a mean of merge weights in [0, 1]; delta a ratio of norms of bf16 states
 IMP_ABS_TOL = 1e-4
 DELTA_REL_TOL = 2e-2
@@ -45,19 +54,36 @@ def masks_from_planners(w: W.Workload, step: int = 0):
     return m1, m2, c1, c2
 
 
+def row_bound(ref: np.ndarray) -> np.ndarray:
+    """Per-element bound 2^-6 max_d |ref[r, h, :]| + 1e-6 for outputs ref [n, H, D]."""
+    return O_ROW_REL_TOL * np.abs(ref).max(axis=-1, keepdims=True) + O_ROW_ABS_FLOOR
+
+
+def assert_rows_close(got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
+    """Element-wise O check of states or outputs [..., H, D]: the absolute 1e-2 of the target
+    and the row-scaled bound; returns the largest ratio to the row bound."""
+    d = np.abs(got - ref)
+    ratio = float((d / row_bound(ref)).max()) if d.size else 0.0
+    assert d.max() <= O_ABS_TOL, f"{what}: max|dO| {d.max():.3e}"
+    assert ratio <= 1.0, f"{what}: {int((d > row_bound(ref)).sum())} elements beyond the row bound (ratio {ratio:.3f})"
+    return ratio
+
+
 @dataclasses.dataclass
 class Compare:
     o_abs: float
     o_rel_fro: float
     lse_abs: float
     o_abs_exact: float
+    o_row_ratio: float        # max over elements of |dO| / row_bound(O_ref)
 
     def ok(self) -> bool:
-        return self.o_abs <= O_ABS_TOL and self.lse_abs <= LSE_ABS_TOL and self.o_rel_fro <= O_REL_FRO_TOL
+        return (self.o_abs <= O_ABS_TOL and self.lse_abs <= LSE_ABS_TOL and self.o_rel_fro <= O_REL_FRO_TOL
+                and self.o_row_ratio <= 1.0)
 
     def __str__(self):
         return (f"max|dO|={self.o_abs:.3e} (vs exact states {self.o_abs_exact:.3e}) "
-                f"relF={self.o_rel_fro:.3e} max|dlse|={self.lse_abs:.3e}")
+                f"relF={self.o_rel_fro:.3e} max|dlse|={self.lse_abs:.3e} row-bound ratio={self.o_row_ratio:.3f}")
 
 
 def compare_out(gpu_O: np.ndarray, gpu_lse: np.ndarray, res: oracle.StepResult) -> Compare:
@@ -66,10 +92,12 @@ def compare_out(gpu_O: np.ndarray, gpu_lse: np.ndarray, res: oracle.StepResult) 
     fin = np.isfinite(res.lse_stored)
     dl = np.abs(np.where(fin, gpu_lse - res.lse_stored, 0.0))
     assert np.array_equal(np.isfinite(gpu_lse), fin), "lse finiteness differs"
-    return Compare(o_abs=float(np.abs(gpu_O - ref).max()),
+    dO = np.abs(gpu_O - ref)
+    return Compare(o_abs=float(dO.max()),
                    o_rel_fro=float(np.linalg.norm(gpu_O - ref) / max(np.linalg.norm(ref), 1e-300)),
                    lse_abs=float(dl.max()) if dl.size else 0.0,
-                   o_abs_exact=float(np.abs(gpu_O - res.O).max()))
+                   o_abs_exact=float(np.abs(gpu_O - res.O).max()),
+                   o_row_ratio=float((dO / row_bound(ref)).max()))
 
 
 class GpuRun:

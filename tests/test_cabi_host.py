@@ -103,9 +103,31 @@ def test_attention_grid_beyond_32_bit_work_items(L):
     assert _call(L, S_q=S_q, S_kv=64, H=40, D=128, qo=(0, S_q), ko=tuple(range(65)), rec=(1,) * 64) == -2
 
 
-def test_head_width_beyond_a_tile_buffer_range(L):
-    """H*D above 2^25: 32 key rows of a tile would not fit one 31-bit buffer range."""
-    assert _call(L, H=(1 << 25) // 64 + 1, D=64) == -2
+def _tile_span_limit(D):
+    """Largest H*D whose 32-key tile rows (31 row strides of H*D bf16 plus one row of D)
+    fit a 31-bit buffer range, and H*D must be a multiple of D."""
+    return ((2 ** 31 - 1) // 2 - D) // 31 // D * D
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_head_width_at_the_tile_buffer_range(L, D):
+    """The shape check of the attention calls passes at the largest H for D and fails one
+    head above it.  An accepted shape is shown by the next check failing instead (delta
+    requested without a workspace: DIT_ERR_WORKSPACE), so no kernel is launched."""
+    H = _tile_span_limit(D) // D
+    assert (31 * H * D + D) * 2 <= 2 ** 31 - 1 < (31 * (H + 1) * D + D) * 2
+    assert _call(L, H=H, D=D, delta=1) == -6
+    assert _call(L, H=H + 1, D=D, delta=1) == -2
+    # 2^25 (accepted) and 2^25 - 64 (accepted); the merge does not build a tile descriptor
+    for hd in (1 << 25, (1 << 25) - 64):
+        assert _call(L, H=hd // 64, D=64, delta=1) == -6
+
+
+def test_merge_does_not_apply_the_tile_range_limit(L):
+    """Only the attention calls copy K/V tiles: a merge with H*D above the tile limit passes
+    the shape check (it fails later, on a NULL output pointer)."""
+    H = _tile_span_limit(128) // 128 + 1
+    assert L.dit_state_merge(1, 1, 1, 8, H, 128, 2, None, 1, None) == -1
 
 
 def test_too_many_blocks_or_partitions(L):
@@ -124,15 +146,25 @@ def _u8(s):
 
 
 @pytest.mark.parametrize("call,code", [
-    # dit_partition_attention_fp8(q, k, v, B, S_q, S_kv, H, D, qo, n_qb, ko, P, local, rec, q8, scale, lse, sm, ws, wsb, st)
+    # dit_partition_attention_fp8(q, k, v, B, S_q, S_kv, H, D, qo, n_qb, ko, P, local, rec, valid, q8, scale, lse,
+    #                             sm, ws, wsb, st)
     (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
-                                             _u8([1, 0]), 1, None, 1, 0.0, None, 0, None), -1),
+                                             _u8([1, 0]), None, 1, None, 1, 0.0, None, 0, None), -1),
     (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 96, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
-                                             _u8([1, 0]), 1, 1, 1, 0.0, None, 0, None), -7),
+                                             _u8([1, 0]), None, 1, 1, 1, 0.0, None, 0, None), -7),
     (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 5, 4]), 2, _i32([0]),
-                                             _u8([1, 0]), 1, 1, 1, 0.0, None, 0, None), -3),
+                                             _u8([1, 0]), None, 1, 1, 1, 0.0, None, 0, None), -3),
     (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
-                                             _u8([0, 1]), 1, 1, 1, 0.0, None, 0, None), -4),
+                                             _u8([0, 1]), None, 1, 1, 1, 0.0, None, 0, None), -4),
+    # the compressed cache refuses reuse of a never-computed slot itself
+    (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
+                                             _u8([1, 0]), _u8([1, 0]), 1, 1, 1, 0.0, None, 0, None), -5),
+    # ... and a delta against a never-computed local slot
+    (lambda L: L.dit_partition_attention_fp8(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
+                                             _u8([1, 1]), _u8([0, 1]), 1, 1, 1, 0.0, 1, 1 << 20, None), -5),
+    # dit_partition_attention(q, k, v, B, S_q, S_kv, H, D, qo, n_qb, ko, P, local, rec, valid, o, lse, sm, ws, wsb, st)
+    (lambda L: L.dit_partition_attention(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
+                                         _u8([1, 0]), _u8([1, 0]), 1, 1, 0.0, None, 0, None), -5),
     # dit_state_merge_fp8(q8, scale, lse, B, S_q, H, D, P, out, lse_out, st)
     (lambda L: L.dit_state_merge_fp8(1, None, 1, 1, 8, 1, 64, 2, 1, 1, None), -1),
     (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 64, 65, 1, 1, None), -2),

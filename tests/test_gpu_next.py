@@ -31,12 +31,12 @@ def test_group_compose_then_continue_at_group_level():
     cO, cL = oracle.compose_states(o.cache.stored_O, o.cache.stored_lse, go)
     gO = PT.bf16_to_f64(sa2.cache_o[:, 0])
     gL = sa2.cache_lse[:, 0].double().cpu().numpy()
-    assert np.abs(gO - cO).max() <= PT.O_ABS_TOL
+    PT.assert_rows_close(gO, cO, "composed planes")
     assert np.linalg.norm(gO - cO) / np.linalg.norm(cO) <= PT.O_REL_FRO_TOL
     assert np.abs(gL - cL).max() <= PT.LSE_ABS_TOL
     # and against the state of the union computed directly (no recomputation needed)
     ue = oracle.compose_states(o.cache.exact_O, o.cache.exact_lse, go)
-    assert np.abs(gO - ue[0]).max() <= PT.O_ABS_TOL
+    PT.assert_rows_close(gO, ue[0], "composed planes vs union states")
     # one more step at group granularity: 4 of 8 groups recomputed by distance
     G = len(go) - 1
     local_g = [i // 2 for i in range(w.n_qb)]
@@ -94,7 +94,7 @@ def test_overlapped_step_matches_oracle():
     Os = [np.where(sel[p][:, None, None], o.cache.stored_O[p], 0.0) for p in range(w.P)]
     Ls = [np.where(sel[p][None, :], o.cache.stored_lse[p], -np.inf) for p in range(w.P)]
     rO, rL = oracle.merge_states(Os, Ls)
-    assert np.abs(pO - rO).max() <= PT.O_ABS_TOL
+    PT.assert_rows_close(pO, rO, "partial state of the reused planes")
 
 
 def test_masked_merge_selects_planes_per_block():

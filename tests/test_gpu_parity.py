@@ -53,7 +53,7 @@ def run_single_step(w, rows=None, want_delta=True, want_importance=True):
             fin = np.isfinite(ref_l)
             assert np.array_equal(np.isfinite(cl[p][:, sel]), fin)
             assert np.abs(np.where(fin, cl[p][:, sel] - ref_l, 0)).max() <= PT.LSE_ABS_TOL, p
-            assert np.abs(co[p][sel] - o.cache.stored_O[p][sel]).max() <= PT.O_ABS_TOL, p
+            PT.assert_rows_close(co[p][sel], o.cache.stored_O[p][sel], f"cache slot plane {p}")
     if did and full_rows:
         d_gpu = g.sa.delta[0].cpu().numpy().astype(np.float64)
         d_ref = oracle.local_change(o.local_states(), old_local, rows, w.q_offsets)
@@ -237,7 +237,7 @@ def test_explicit_softmax_scale():
     rows = np.arange(256)
     qd, kd, vd = W.to_f64(X.q[0]), W.to_f64(X.k[0]), W.to_f64(X.v[0])
     O, lse = oracle.full_attention(qd, kd, vd, 0.05)
-    assert np.abs(PT.bf16_to_f64(sa.out[0]) - O).max() <= PT.O_ABS_TOL
+    PT.assert_rows_close(PT.bf16_to_f64(sa.out[0]), O, "explicit scale")
     assert np.abs(sa.lse[0].double().cpu().numpy() - lse).max() <= PT.LSE_ABS_TOL
 
 
@@ -294,5 +294,5 @@ def test_tile_sum_bound_and_maximum_jumps():
     sa.step(*(PT.to_dev(b) for b in bits), np.ones((1, 1), np.uint8))
     torch.cuda.synchronize()
     O, lse = oracle.full_attention(qd, kd, vd, 1.0 / sq)
-    assert np.abs(PT.bf16_to_f64(sa.out[0]) - O).max() <= PT.O_ABS_TOL
+    PT.assert_rows_close(PT.bf16_to_f64(sa.out[0]), O, "tile-sum bound")
     assert np.abs(sa.lse[0].double().cpu().numpy() - lse).max() <= PT.LSE_ABS_TOL
