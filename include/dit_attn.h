@@ -62,6 +62,9 @@ extern "C" {
 
 #define DIT_MAX_BLOCKS 64
 #define DIT_MAX_PARTITIONS 64
+/* Bytes of the device scratch that dit_attn_partitioned_noalloc uses in place of a
+ * workspace (one array per GPU the library runs on, held until the process ends). */
+#define DIT_SCRATCH_BYTES (1u << 20)
 
 typedef enum {
   DIT_OK = 0,
@@ -118,6 +121,36 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v,
                          float *delta_out,
                          void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/*
+ * dit_attn_partitioned for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and errors as dit_attn_partitioned, without the workspace: the local-change partial sums
+ * go to a device array inside the library, DIT_SCRATCH_BYTES per GPU (file-scope device
+ * memory, held until the process ends; its address is looked up once per device, on the
+ * first call that needs it with that device current).  The call allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.
+ *   - delta_out given and dit_attn_workspace_bytes(...) > DIT_SCRATCH_BYTES:
+ *     DIT_ERR_WORKSPACE (e.g. B = 1, H = 40 allows about 3,270 query tiles of 128 rows
+ *     plus blocks, S_q up to ~410,000 rows).
+ *   - The array keeps the last call's contents; every entry a call reads is written by the
+ *     same call, so nothing needs clearing.  Calls that overlap on one GPU (on different
+ *     streams, or from different threads) share the array and race: serialise them.
+ *   - Unlike the other calls this one keeps state across calls (the per-device address).
+ */
+int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v,
+                                 int B, int S_q, int S_kv, int H, int D,
+                                 const int32_t *q_offsets, int n_qb,
+                                 const int32_t *kv_offsets, int P,
+                                 const int32_t *local_part,
+                                 const uint8_t *recompute,
+                                 const uint8_t *cache_valid,
+                                 void *cache_o, float *cache_lse,
+                                 void *out, float *lse,
+                                 float softmax_scale,
+                                 float *importance_out,
+                                 float *delta_out,
+                                 void *stream);
 
 /*
  * Partition attention and cache update only: for every (i, p) with recompute = 1, compute

@@ -26,6 +26,10 @@ SIGNATURES = {
                                      P_i32, c_int, P_i32, c_int, P_i32, P_u8, P_u8,
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dit_attn_partitioned_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                             P_i32, c_int, P_i32, c_int, P_i32, P_u8, P_u8,
+                                             c_void_p, c_void_p, c_void_p, c_void_p, c_float,
+                                             c_void_p, c_void_p, c_void_p]),
     "dit_partition_attention": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                         P_i32, c_int, P_i32, c_int, P_i32, P_u8, P_u8,
                                         c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p]),

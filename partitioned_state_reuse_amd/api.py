@@ -115,6 +115,24 @@ def attn_partitioned(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_l
         wp, ws_bytes, _stream(stream)))
 
 
+def attn_partitioned_noalloc(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, out, lse, *,
+                             local_part=None, cache_valid=None, scale: float = 0.0, importance_out=None,
+                             delta_out=None, stream=None) -> None:
+    """dit_attn_partitioned_noalloc: attn_partitioned with the library's own device scratch
+    in place of a workspace (for callers that cannot allocate)."""
+    (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
+    n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
+    _check(_lib.lib().dit_attn_partitioned_noalloc(
+        qp, kp, vp, B, S_q, S_kv, H, D,
+        _i32(q_offsets), n_qb, _i32(kv_offsets), P,
+        None if local_part is None else _i32(local_part), _u8(recompute),
+        None if cache_valid is None else _u8(cache_valid),
+        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"),
+        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), float(scale),
+        _dev(importance_out, F32, (B, n_qb, P), "importance_out"), _dev(delta_out, F32, (B, n_qb), "delta_out"),
+        _stream(stream)))
+
+
 def partition_attention(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, *,
                         local_part=None, cache_valid=None, scale: float = 0.0, delta_partials=None,
                         stream=None) -> None:

@@ -373,4 +373,26 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v, int B, int
                          workspace, workspace_bytes, stream);
 }
 
+int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H,
+                                 int D, const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P,
+                                 const int32_t *local_part, const uint8_t *recompute, const uint8_t *cache_valid,
+                                 void *cache_o, float *cache_lse, void *out, float *lse, float softmax_scale,
+                                 float *importance_out, float *delta_out, void *stream) {
+  try {
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if (delta_out != nullptr) {
+      // the library's own device scratch stands in for the workspace (sizes beyond it are
+      // rejected by the workspace check, DIT_ERR_WORKSPACE)
+      if (dit::scratch_address(&ws) != hipSuccess) return DIT_ERR_HIP;
+      ws_bytes = dit::kScratchBytes;
+    }
+    return run_partitioned(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
+                           cache_valid, cache_o, cache_lse, out, lse, softmax_scale, importance_out, delta_out, ws,
+                           ws_bytes, stream);
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
 }  // extern "C"

@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "launch.h"
@@ -1116,6 +1117,34 @@ hipError_t launch_delta_finalize(const float *partials, int B, int H, const Bloc
   dim3 grid((unsigned)blocks.n_qb, (unsigned)B), block(256);
   hipLaunchKernelGGL(delta_finalize_kernel, grid, block, 0, stream, partials, H, blocks, delta_out);
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free entry point.  Each GPU holds its own copy at its own
+// address; in host code `scratch` names a host-side stand-in, so kernels get the device
+// address from hipGetSymbolAddress instead, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dit

@@ -108,4 +108,10 @@ hipError_t launch_importance(const float *cache_lse, const float *lse, int B, in
 hipError_t launch_delta_finalize(const float *partials, int B, int H, const BlockDesc &blocks,
                                  float *delta_out, hipStream_t stream);
 
+// Device scratch of the allocation-free entry point: a file-scope device array of
+// kScratchBytes in kernels.hip.  scratch_address gives its address on the current device
+// (looked up once per device with hipGetSymbolAddress, then cached).
+constexpr size_t kScratchBytes = DIT_SCRATCH_BYTES;
+hipError_t scratch_address(void **out);
+
 }  // namespace dit

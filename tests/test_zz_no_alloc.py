@@ -1,0 +1,96 @@
+"""GPU test of dit_attn_partitioned_noalloc (the allocation-free variant of
+dit_attn_partitioned, with the library's own device scratch in place of the workspace),
+called through the C ABI: two calls in a row, the second on a smaller input, each against
+dit_attn_partitioned on the same inputs and the same starting cache."""
+import ctypes
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import workloads as W
+import _parity as PT
+from partitioned_state_reuse_amd import _lib, api
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _one_case(w, mask_seed):
+    """Fill a cache by an all-recompute step on X_prev, copy it, then run the selective step
+    with importance and local change through both entry points."""
+    X, Xp = W.make_step(w, 0), W.make_step(w, -1)
+    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
+    base = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part)
+    base.step(PT.to_dev(Xp.q), PT.to_dev(Xp.k), PT.to_dev(Xp.v), np.ones((w.n_qb, w.P), np.uint8))
+    rng = np.random.default_rng(mask_seed)
+    mask = (rng.random((w.n_qb, w.P)) < 0.5).astype(np.uint8)
+    for i, lp in enumerate(w.local_part):
+        mask[i, lp] = 1
+    valid = np.ones((w.n_qb, w.P), np.uint8)
+    outs = {}
+    for name in ("workspace", "noalloc"):
+        co, cl = base.cache_o.clone(), base.cache_lse.clone()
+        out = torch.full_like(base.out, float("nan"))
+        lse = torch.full_like(base.lse, float("nan"))
+        imp = torch.full_like(base.importance, float("nan"))
+        dl = torch.full_like(base.delta, float("nan"))
+        kw = dict(local_part=w.local_part, cache_valid=valid, importance_out=imp, delta_out=dl)
+        if name == "workspace":
+            ws = torch.empty_like(base.workspace)
+            api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, mask, co, cl, out, lse, workspace=ws, **kw)
+        else:
+            api.attn_partitioned_noalloc(q, k, v, w.q_offsets, w.kv_offsets, mask, co, cl, out, lse, **kw)
+        torch.cuda.synchronize()
+        outs[name] = (out, lse, imp, dl, co, cl)
+    a, b = outs["workspace"], outs["noalloc"]
+    for x, y, what in zip(a, b, ("out", "lse", "importance", "delta", "cache_o", "cache_lse")):
+        assert torch.equal(x, y), what
+    assert torch.isfinite(a[3]).all() and torch.isfinite(a[2]).all()
+    _log(f"{w.name} S_q={w.S_q} H={w.H}: no-alloc step equal to the workspace step "
+         f"(delta {a[3][0, :3].tolist()})")
+
+
+def test_noalloc_matches_workspace_entry_point_twice_second_smaller():
+    big = W.workload("video720p", grid=(5, 18, 32), H=4)
+    small = W.workload("tiny")
+    assert small.S_q * small.H < big.S_q * big.H
+    _one_case(big, 1)
+    _one_case(small, 2)
+
+
+def test_noalloc_without_local_change():
+    w = W.workload("tiny")
+    X = W.make_step(w, 0)
+    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
+    sa = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part)
+    ones = np.ones((w.n_qb, w.P), np.uint8)
+    sa.step(q, k, v, ones)
+    out, lse = torch.empty_like(sa.out), torch.empty_like(sa.lse)
+    co, cl = torch.empty_like(sa.cache_o), torch.empty_like(sa.cache_lse)
+    api.attn_partitioned_noalloc(q, k, v, w.q_offsets, w.kv_offsets, ones, co, cl, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, sa.out) and torch.equal(lse, sa.lse)
+
+
+def test_noalloc_rejects_sizes_beyond_the_scratch():
+    """Validation on the host: a local-change request whose partial sums exceed the scratch
+    is DIT_ERR_WORKSPACE (the fake device pointers are never dereferenced)."""
+    L = _lib.lib()
+    H, D = 40, 128
+    S_q = 600_000                                     # (4688 tiles + 1) * 40 * 8 B > 1 MiB
+    assert L.dit_attn_workspace_bytes(1, S_q, H, D, 1, 2) > (1 << 20)
+    i32 = lambda s: (ctypes.c_int32 * len(s))(*s)
+    u8 = lambda s: (ctypes.c_uint8 * len(s))(*s)
+    rc = L.dit_attn_partitioned_noalloc(16, 16, 16, 1, S_q, 64, H, D, i32([0, S_q]), 1, i32([0, 32, 64]), 2,
+                                        i32([0]), u8([1, 0]), None, 16, 16, 16, 16, 0.0, None, 16, None)
+    assert rc == -6
+    S_q = 200_000                                     # fits: rejected later, for the NULL q
+    assert L.dit_attn_workspace_bytes(1, S_q, H, D, 1, 2) <= (1 << 20)
+    rc = L.dit_attn_partitioned_noalloc(None, 16, 16, 1, S_q, 64, H, D, i32([0, S_q]), 1, i32([0, 32, 64]), 2,
+                                        i32([0]), u8([1, 0]), None, 16, 16, 16, 16, 0.0, None, 16, None)
+    assert rc == -1
