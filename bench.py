@@ -52,47 +52,6 @@ def merge_bytes(w: W.Workload) -> float:
     return float(w.S_q * w.H * (w.P * (2 * w.D + 4) + (2 * w.D + 4)))
 
 
-def cpu_baseline(w: W.Workload, X: "W.StepInputs", mask: np.ndarray, rows_per_block: int) -> dict:
-    """Time the oracle's step work (recomputed partition states + merge) on a row sample."""
-    import oracle
-    try:
-        affinity = len(os.sched_getaffinity(0))
-    except AttributeError:
-        affinity = os.cpu_count() or 1
-    # the oracle's parallel work is its BLAS matrix products: report that pool's thread count
-    threads = affinity
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [d["num_threads"] for d in threadpool_info() if d.get("user_api") == "blas"]
-        if blas:
-            threads = min(max(blas), affinity)
-    except Exception:
-        pass
-    rows = np.concatenate([np.arange(w.q_offsets[i], w.q_offsets[i] + min(rows_per_block, w.q_offsets[i + 1] - w.q_offsets[i]))
-                           for i in range(w.n_qb)])
-    q = W.to_f64(X.q[0][rows])
-    k = W.to_f64(X.k[0])
-    v = W.to_f64(X.v[0])
-    cache = oracle.StateCache.empty(rows, w.P, w.H, w.D, w.n_qb)
-    # reused slots hold placeholder states: this leg measures time, parity is tested elsewhere
-    sizes = np.diff(w.kv_offsets)
-    for p in range(w.P):
-        cache.exact_lse[p][:] = math.log(max(sizes[p], 1))
-        cache.stored_lse[p][:] = math.log(max(sizes[p], 1))
-    cache.valid[:] = True
-    t0 = time.perf_counter()
-    oracle.selective_step(q, k, v, rows, w.q_offsets, w.kv_offsets, mask, cache, 1.0 / math.sqrt(w.D))
-    dt = time.perf_counter() - t0
-    blk = oracle.block_of_rows(rows, w.q_offsets)
-    flop = float(4 * w.D * w.H * sum(int(mask[b].astype(np.int64) @ sizes) for b in blk))
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "host_cpus_available": affinity,
-            "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"{len(rows)} of {w.S_q} query rows (first {rows_per_block} of each of the {w.n_qb} "
-                      f"query blocks), all {w.H} heads: fp64 states of the recomputed partitions and the "
-                      f"{w.P}-state merge; reused slots hold placeholder states"}
-
-
 def kernel_source_sha256() -> str:
     import hashlib
     d = os.path.join(ROOT, "partitioned_state_reuse_amd", "csrc")
@@ -221,34 +180,77 @@ def run_trajectory(args, w: "W.Workload") -> dict:
     }
 
 
-def main() -> int:
-    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profile":
-        print(summarize_profile(sys.argv[2]))
-        return 0
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="video720p", choices=["video720p", "share32", "image_anchor", "longvideo"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=64, help="oracle sample rows per query block")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1 "
-                                   "(the path would shard by query block across GPUs; that exchange is not implemented)"}))
-        return 2
+def evict_cache(buf) -> None:
+    """Overwrite a buffer larger than the 256 MB Infinity Cache (MALL) so that a following
+    kernel reads its inputs from HBM, not from data the previous kernel left in the MALL."""
+    buf.fill_(1)
 
+
+def oracle_leg(w: W.Workload, X: "W.StepInputs", Xp: "W.StepInputs", mask: np.ndarray, rows: np.ndarray,
+               gpu_out: np.ndarray, gpu_lse: np.ndarray) -> dict:
+    """The oracle beside the GPU step: its reused slots hold the previous step's states for the
+    sampled rows (computed first, not timed), then its step work (states of the recomputed
+    partitions and the merge of all P states) is timed; the GPU output on the same rows is
+    checked against it to the tolerances of the tests."""
+    import oracle
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    # the oracle's parallel work is its BLAS matrix products: report that pool's thread count
+    threads = affinity
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [d["num_threads"] for d in threadpool_info() if d.get("user_api") == "blas"]
+        if blas:
+            threads = min(max(blas), affinity)
+    except Exception:
+        pass
+    scale = 1.0 / math.sqrt(w.D)
+    cache = oracle.StateCache.empty(rows, w.P, w.H, w.D, w.n_qb)
+    cache.valid[:] = True          # slots not computed yet hold empty states (weight 0)
+    t0 = time.perf_counter()
+    oracle.selective_step(W.to_f64(Xp.q[0][rows]), W.to_f64(Xp.k[0]), W.to_f64(Xp.v[0]), rows, w.q_offsets,
+                          w.kv_offsets, 1 - mask, cache, scale)
+    prep = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    res = oracle.selective_step(W.to_f64(X.q[0][rows]), W.to_f64(X.k[0]), W.to_f64(X.v[0]), rows, w.q_offsets,
+                                w.kv_offsets, mask, cache, scale)
+    dt = time.perf_counter() - t0
+    blk = oracle.block_of_rows(rows, w.q_offsets)
+    sizes = np.diff(w.kv_offsets)
+    flop = float(4 * w.D * w.H * sum(int(mask[b].astype(np.int64) @ sizes) for b in blk))
+    ref, fin = res.O_stored, np.isfinite(res.lse_stored)
+    dO = np.abs(gpu_out - ref)
+    row_bound = 2.0 ** -6 * np.abs(ref).max(axis=-1, keepdims=True) + 1e-6
+    parity = {"rows": int(len(rows)),
+              "max_abs_O": float(dO.max()),
+              "rel_fro_O": float(np.linalg.norm(gpu_out - ref) / np.linalg.norm(ref)),
+              "max_abs_lse": float(np.abs(np.where(fin, gpu_lse - res.lse_stored, 0.0)).max()),
+              "row_bound_ratio": float((dO / row_bound).max())}
+    parity["ok"] = bool(parity["max_abs_O"] <= 1e-2 and parity["rel_fro_O"] <= 1e-2 and
+                        parity["max_abs_lse"] <= 1e-3 and parity["row_bound_ratio"] <= 1.0 and
+                        np.array_equal(np.isfinite(gpu_lse), fin))
+    full = len(rows) == w.S_q
+    out = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "host_cpus_available": affinity,
+           "kind": "oracle", "seconds": round(dt, 3), "prep_seconds": round(prep, 3)}
+    if full:
+        out["sample"] = (f"all {w.S_q} query rows, all {w.H} heads (the whole step): fp64 states of the "
+                         f"{int(mask.sum())} recomputed (block, partition) pairs and the {w.P}-state merge; "
+                         f"reused slots hold the previous step's states (computed before the timing)")
+    else:
+        out["sample"] = (f"{len(rows)} of {w.S_q} query rows (the first and the last 128-row tile of each of "
+                         f"the {w.n_qb} query blocks), all {w.H} heads: fp64 states of the recomputed "
+                         f"partitions and the {w.P}-state merge; reused slots hold the previous step's states "
+                         f"(computed before the timing)")
+        out["extrapolated_step_s"] = round(dt * w.S_q / len(rows), 2)
+    return out, parity
+
+
+def layer_bench(w: W.Workload, args, dev, evict_buf, extras: bool) -> dict:
+    """Time the selective step of one single-step layer and its two kernels."""
     import torch
     from partitioned_state_reuse_amd import api
-
-    if not torch.cuda.is_available():
-        log("no GPU visible")
-        return 1
-    dev = torch.device("cuda:0")
-    w = W.workload(args.workload)
-    if w.mode == "wdelta":
-        print(json.dumps(run_trajectory(args, w)), flush=True)
-        return 0
     log(f"[bench] workload {w.name}: S_q={w.S_q} S_kv={w.S_kv} H={w.H} D={w.D} P={w.P} n_qb={w.n_qb}")
     t0 = time.time()
     X = W.make_step(w, 0)
@@ -269,24 +271,22 @@ def main() -> int:
     torch.cuda.synchronize()
     del qp, kp, vp
     stream = torch.cuda.current_stream()
-    want_delta = True
-    n_ev = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    valid = np.ones((w.n_qb, w.P), np.uint8)
 
     def one_step(t, events=None):
         mask, _ = planner.next(t)
         if events:
             events[0].record(stream)
         api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
-                                local_part=w.local_part, delta_partials=sa.workspace if want_delta else None,
+                                local_part=w.local_part, cache_valid=valid, workspace=sa.workspace,
                                 stream=stream)
         if events:
             events[1].record(stream)
         api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
         if events:
             events[2].record(stream)
-        if want_delta:
-            api.local_change_finalize(sa.workspace, 1, w.S_q, w.H, w.D, w.q_offsets, sa.delta, stream=stream)
+        api.local_change_finalize(sa.workspace, 1, w.S_q, w.H, w.D, w.q_offsets, sa.delta, stream=stream)
         if events:
             events[3].record(stream)
         return mask
@@ -301,19 +301,107 @@ def main() -> int:
     wall = time.perf_counter() - t_start
     ms_step = wall / max(args.steps, 1) * 1e3
     attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    merge_in_step_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     fin_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    # the GPU's output of the step, for the parity check beside the oracle
+    rows = np.arange(w.S_q) if w.S_q <= 4096 else W.sample_rows(w, tiles_per_block=2, tile=128)
+    ridx = torch.as_tensor(rows, device=dev)
+    gpu_out = W.to_f64(sa.out[0, ridx].view(torch.int16).cpu().numpy().view(np.uint16))
+    gpu_lse = sa.lse[0][:, ridx].double().cpu().numpy()
+
+    # the merge alone, each launch after an overwrite of the Infinity Cache
+    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in mev:
+        evict_cache(evict_buf)
+        e[0].record(stream)
+        api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    merge_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
+
     flop = attn_flop(w, mask)
     mbytes = merge_bytes(w)
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
-    # clock under load and MFMA busy fraction from the committed counter record (None when stale)
-    attn_counters = measured_counters(w.name)
     merge_gbs = mbytes / (merge_ms * 1e-3) / 1e9
-    log(f"[bench] step {ms_step:.3f} ms  attention {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s)  "
-        f"merge {merge_ms:.3f} ms ({merge_gbs:.0f} GB/s)  finalize {fin_ms:.4f} ms")
+    log(f"[bench] {w.name}: step {ms_step:.3f} ms  attention {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s)  "
+        f"merge {merge_ms:.3f} ms after MALL eviction ({merge_gbs:.0f} GB/s; in the step {merge_in_step_ms:.3f} ms)  "
+        f"finalize {fin_ms:.4f} ms")
+    traffic = measured_traffic(w.name)
+    attn_counters = measured_counters(w.name)
+    merge_kernel = f"state_merge_kernel<128, {16 if w.P <= 16 else 32 if w.P <= 32 else 64}>"
+    res = {
+        "ms_per_step": round(ms_step, 4),
+        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "config": {"workload": w.name, "tokens": w.S_kv, "query_tokens": w.S_q, "heads": w.H, "head_dim": w.D,
+                   "partitions": w.P, "query_blocks": w.n_qb, "group_size": int(np.diff(w.group_offsets)[0]),
+                   "recomputed_groups_per_block": w.recompute_groups,
+                   "recomputed_pairs": int(mask.sum()), "reused_pairs": int(mask.size - mask.sum()),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic.get("dit::partition_attention_kernel<128, false>"),
+                     "kernel": "partition_attention_kernel<128, false>", "ms": round(attn_ms, 4),
+                     "algorithmic_flop": flop, "counters": attn_counters or None,
+                     "frac_of_clock_peak": (round(attn_tflops / attn_counters["peak_tflops_at_that_clock"], 4)
+                                            if attn_counters else None)},
+        "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
+                           "traffic": traffic.get("dit::" + merge_kernel),
+                           "kernel": merge_kernel, "ms": round(merge_ms, 4), "ms_in_step": round(merge_in_step_ms, 4),
+                           "algorithmic_bytes": mbytes, "timing": "each launch after a 1 GiB overwrite of the MALL"},
+        "local_change_finalize_ms": round(fin_ms, 5),
+    }
+    ctx = {"X": X, "Xp": Xp, "mask": mask, "rows": rows, "gpu_out": gpu_out, "gpu_lse": gpu_lse,
+           "q": q, "k": k, "v": v, "sa": sa, "planner": planner, "flop": flop, "ms_step": ms_step,
+           "merge_ms": merge_ms}
+    if extras:
+        res.update(layer_extras(w, args, dev, ctx, evict_buf))
+    else:
+        ov_ms = overlapped_step_ms(args, ctx)
+        log(f"[bench] {w.name}: overlapped step {ov_ms:.3f} ms (plain {ms_step:.3f})")
+        res["overlap_two_streams"] = {"ms_per_step": round(ov_ms, 4), "plain_ms_per_step": round(ms_step, 4),
+                                      "value": round(flop / (ov_ms * 1e-3) / 1e12, 2)}
+    planner.close()
+    return res, ctx
 
-    # a5 importance over this step's states (anchor steps only; timed apart from the step)
+
+def overlapped_step_ms(args, ctx) -> float:
+    """Wall time per step of the two-stream step: the reused states are pre-merged on a second
+    stream during the attention kernel, then merged with the fresh states."""
+    import torch
+    q, k, v, sa, planner, mask = ctx["q"], ctx["k"], ctx["v"], ctx["sa"], ctx["planner"], ctx["mask"]
+    side = torch.cuda.Stream()
+    for _ in range(args.warmup):
+        sa.step_overlapped(q, k, v, mask, side_stream=side, want_delta=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        m_t, _ = planner.next(t + 1)
+        sa.step_overlapped(q, k, v, m_t, side_stream=side, want_delta=True)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
+
+
+def layer_extras(w: W.Workload, args, dev, ctx, evict_buf) -> dict:
+    """Importance, planner and enqueue costs, the two-stream step, group compose and the
+    compressed cache on the same layer."""
+    import torch
+    from partitioned_state_reuse_amd import api
+    q, k, v, sa, planner, flop, mask = ctx["q"], ctx["k"], ctx["v"], ctx["sa"], ctx["planner"], ctx["flop"], ctx["mask"]
+    stream = torch.cuda.current_stream()
+    # a5 importance (anchor steps): inside the merge (partials + a fixed-order finish), timed
+    # like the plain merge after an overwrite of the MALL, and the second pass over the stored
+    # lse planes that callers without a workspace use
     imp = torch.empty((1, w.n_qb, w.P), dtype=torch.float32, device=dev)
+    aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in aev:
+        evict_cache(evict_buf)
+        e[0].record(stream)
+        api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, q_offsets=w.q_offsets, importance_out=imp,
+                        workspace=sa.workspace, stream=stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    anchor_merge_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in aev]))
     api.importance(sa.cache_lse, sa.lse, w.q_offsets, imp, stream=stream)
     i0, i1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     i0.record(stream)
@@ -334,25 +422,25 @@ def main() -> int:
                                 local_part=w.local_part, stream=stream)
     enqueue_us = (time.perf_counter() - t0) / 3 * 1e6
     torch.cuda.synchronize()
-    log(f"[bench] importance {imp_ms:.3f} ms, planner {planner_us:.1f} us/call, attention enqueue {enqueue_us:.1f} us")
+    # the same attention launch without a workspace: every workgroup's item fixed at launch
+    # (no balancing across the XCDs, no local-change partials)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(args.steps):
+        api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse, stream=stream)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    static_ms = s0.elapsed_time(s1) / max(args.steps, 1)
+    log(f"[bench] attention without a workspace (static placement) {static_ms:.3f} ms")
+    log(f"[bench] merge with importance {anchor_merge_ms:.3f} ms (plain {ctx['merge_ms']:.3f}); second-pass importance "
+        f"{imp_ms:.3f} ms, planner {planner_us:.1f} us/call, attention enqueue {enqueue_us:.1f} us")
 
-    # two-stream overlap: the reused states are pre-merged on a second stream during the
-    # attention kernel, then merged with the fresh states
-    side = torch.cuda.Stream()
-    for _ in range(args.warmup):
-        sa.step_overlapped(q, k, v, mask, side_stream=side, want_delta=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(args.steps):
-        m_t, _ = planner.next(t + 1)
-        sa.step_overlapped(q, k, v, m_t, side_stream=side, want_delta=True)
-    torch.cuda.synchronize()
-    ov_ms = (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
+    ov_ms = overlapped_step_ms(args, ctx)
     # dynamic group compose of the P cached states into the groups
     go = w.group_offsets
     G = len(go) - 1
     comp_o = torch.empty((G, 1, w.S_q, w.H, w.D), dtype=torch.bfloat16, device=dev)
-    comp_l = torch.empty((G, 1, w.H, w.S_q), dtype=torch.float32, device=dev)
+    comp_l = torch.empty((G, 1, w.S_q, w.H), dtype=torch.float32, device=dev)
     api.state_compose(sa.cache_o, sa.cache_lse, go, comp_o, comp_l, stream=stream)
     c0_, c1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0_.record(stream)
@@ -363,7 +451,7 @@ def main() -> int:
     comp_ms = c0_.elapsed_time(c1_) / 5
     comp_bytes = float(w.S_q * w.H * (w.P + G) * (2 * w.D + 4))
     del comp_o, comp_l
-    log(f"[bench] overlapped step {ov_ms:.3f} ms (plain {ms_step:.3f}); group compose {comp_ms:.3f} ms "
+    log(f"[bench] overlapped step {ov_ms:.3f} ms (plain {ctx['ms_step']:.3f}); group compose {comp_ms:.3f} ms "
         f"({comp_bytes / (comp_ms * 1e-3) / 1e9:.0f} GB/s)")
 
     # compressed (fp8 e4m3 + per-row-head scale) state cache: same step on its own cache
@@ -371,14 +459,15 @@ def main() -> int:
                                  cache_format="fp8")
     sa8.step(q, k, v, np.ones((w.n_qb, w.P), np.uint8))
     ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    valid = np.ones((w.n_qb, w.P), np.uint8)
 
     def fp8_step(t, e=None):
         m_t, _ = planner.next(t)
         if e:
             e[0].record(stream)
         api.partition_attention_fp8(q, k, v, w.q_offsets, w.kv_offsets, m_t, sa8.cache_o, sa8.cache_scale,
-                                    sa8.cache_lse, local_part=w.local_part, delta_partials=sa8.workspace,
-                                    stream=stream)
+                                    sa8.cache_lse, local_part=w.local_part, cache_valid=valid,
+                                    workspace=sa8.workspace, stream=stream)
         if e:
             e[1].record(stream)
         api.state_merge_fp8(sa8.cache_o, sa8.cache_scale, sa8.cache_lse, sa8.out, sa8.lse, stream=stream)
@@ -395,14 +484,74 @@ def main() -> int:
     torch.cuda.synchronize()
     fp8_ms = (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
     fp8_attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev8]))
-    fp8_merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev8]))
+    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in mev:
+        evict_cache(evict_buf)
+        e[0].record(stream)
+        api.state_merge_fp8(sa8.cache_o, sa8.cache_scale, sa8.cache_lse, sa8.out, sa8.lse, stream=stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    fp8_merge_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
     # per row-head: P planes of D code bytes + scale + lse read, bf16 output + lse written
     fp8_bytes = float(w.S_q * w.H * (w.P * (w.D + 8) + 2 * w.D + 4))
     del sa8
     log(f"[bench] fp8 cache step {fp8_ms:.3f} ms: attention {fp8_attn_ms:.3f} ms, merge {fp8_merge_ms:.3f} ms "
         f"({fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9:.0f} GB/s)")
+    return {
+        "overlap_two_streams": {"ms_per_step": round(ov_ms, 4), "plain_ms_per_step": round(ctx["ms_step"], 4),
+                                "value": round(flop / (ov_ms * 1e-3) / 1e12, 2)},
+        "group_compose": {"ms": round(comp_ms, 4), "gbs": round(comp_bytes / (comp_ms * 1e-3) / 1e9, 1),
+                          "frac": round(comp_bytes / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes": comp_bytes, "planes": f"{w.P} -> {len(w.group_offsets) - 1}"},
+        "fp8_cache": {"ms_per_step": round(fp8_ms, 4), "attention_ms": round(fp8_attn_ms, 4),
+                      "attention_tflops": round(flop / (fp8_attn_ms * 1e-3) / 1e12, 1),
+                      "merge_ms": round(fp8_merge_ms, 4),
+                      "merge_gbs": round(fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9, 1),
+                      "merge_frac": round(fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "merge_algorithmic_bytes": fp8_bytes,
+                      "value": round(flop / (fp8_ms * 1e-3) / 1e12, 2)},
+        "anchor_merge": {"ms": round(anchor_merge_ms, 4), "plain_merge_ms": round(ctx["merge_ms"], 4),
+                         "gbs": round(merge_bytes(w) / (anchor_merge_ms * 1e-3) / 1e9, 1),
+                         "what": "merge with the importance partials and their fixed-order finish (two launches)"},
+        "importance_second_pass_ms": round(imp_ms, 4),
+        "attention_static_placement_ms": round(static_ms, 4),
+        "planner_us_per_step": round(planner_us, 2),
+        "attention_enqueue_us": round(enqueue_us, 2),
+    }
+
+
+def main() -> int:
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profile":
+        print(summarize_profile(sys.argv[2]))
+        return 0
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="video720p", choices=["video720p", "share32", "image_anchor", "longvideo"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-share32", action="store_true", help="with the 720p layer: skip the 32-way-share object")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1 "
+                                   "(the path would shard by query block across GPUs; that exchange is not implemented)"}))
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    dev = torch.device("cuda:0")
+    w = W.workload(args.workload)
+    if w.mode == "wdelta":
+        print(json.dumps(run_trajectory(args, w)), flush=True)
+        return 0
+    evict_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    layer, ctx = layer_bench(w, args, dev, evict_buf, extras=(w.name == "video720p"))
 
     # plain device copy of 4 GiB as the achievable-bandwidth reference (and PMC calibration)
+    stream = torch.cuda.current_stream()
     src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -415,61 +564,44 @@ def main() -> int:
     copy_gbs = 3 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
     log(f"[bench] device copy {copy_gbs:.0f} GB/s")
+    layer["roofline_merge"]["device_copy_gbs"] = round(copy_gbs, 1)
 
-    traffic = measured_traffic(w.name)
-    attn_traffic = traffic.get("dit::partition_attention_kernel<128, false>")
-    merge_traffic = traffic.get(f"dit::state_merge_kernel<128, {16 if w.P <= 16 else 32 if w.P <= 32 else 64}>")
+    share = None
+    if w.name == "video720p" and not args.no_share32:
+        ws = W.workload("share32")
+        share, sctx = layer_bench(ws, args, dev, evict_buf, extras=False)
+        share["metric"] = "recomputed-attn TFLOP/s + merge GB/s, one GPU's share of a 32-way split of 75.6k tokens"
+        share["unit"] = "TFLOP/s"
+    del evict_buf
     result = {
         "metric": "recomputed-attn TFLOP/s + merge GB/s at 75.6k tokens, % of MFMA/HBM peak",
-        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "value": layer["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": layer["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) Q/K/V with 3D RoPE, bf16",
-        "config": {"workload": w.name, "tokens": w.S_kv, "query_tokens": w.S_q, "heads": w.H, "head_dim": w.D,
-                   "partitions": w.P, "query_blocks": w.n_qb, "group_size": int(np.diff(w.group_offsets)[0]),
-                   "recomputed_groups_per_block": w.recompute_groups,
-                   "recomputed_pairs": int(mask.sum()), "reused_pairs": int(mask.size - mask.sum()),
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic,
-                     "kernel": "partition_attention_kernel<128, false>", "ms": round(attn_ms, 4),
-                     "algorithmic_flop": flop, "counters": attn_counters or None,
-                     "frac_of_clock_peak": (round(attn_tflops / attn_counters["peak_tflops_at_that_clock"], 4)
-                                            if attn_counters else None)},
-        "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
-                           "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4), "traffic": merge_traffic,
-                           "kernel": "state_merge_kernel<128,16>", "ms": round(merge_ms, 4),
-                           "algorithmic_bytes": mbytes, "device_copy_gbs": round(copy_gbs, 1)},
-        "local_change_finalize_ms": round(fin_ms, 5),
-        "overlap_two_streams": {"ms_per_step": round(ov_ms, 4), "plain_ms_per_step": round(ms_step, 4),
-                                "value": round(flop / (ov_ms * 1e-3) / 1e12, 2)},
-        "group_compose": {"ms": round(comp_ms, 4), "gbs": round(comp_bytes / (comp_ms * 1e-3) / 1e9, 1),
-                          "frac": round(comp_bytes / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                          "algorithmic_bytes": comp_bytes, "planes": f"{w.P} -> {len(w.group_offsets) - 1}"},
-        "fp8_cache": {"ms_per_step": round(fp8_ms, 4), "attention_ms": round(fp8_attn_ms, 4),
-                      "attention_tflops": round(flop / (fp8_attn_ms * 1e-3) / 1e12, 1),
-                      "merge_ms": round(fp8_merge_ms, 4),
-                      "merge_gbs": round(fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9, 1),
-                      "merge_frac": round(fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                      "merge_algorithmic_bytes": fp8_bytes,
-                      "value": round(flop / (fp8_ms * 1e-3) / 1e12, 2)},
-        "importance_ms": round(imp_ms, 4),
-        "importance_gbs": round(float(w.S_q * w.H * w.P * 8) / (imp_ms * 1e-3) / 1e9, 1),
-        "planner_us_per_step": round(planner_us, 2),
-        "attention_enqueue_us": round(enqueue_us, 2),
     }
+    result.update({k: v for k, v in layer.items() if k not in ("value", "ms_per_step")})
     if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on a row sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, X, mask, args.cpu_rows)
-        log(f"[bench] oracle {result['cpu_baseline']['seconds']} s")
-    planner.close()
+        log(f"[bench] timing the oracle on {len(ctx['rows'])} rows of {w.name} ...")
+        result["cpu_baseline"], result["parity"] = oracle_leg(w, ctx["X"], ctx["Xp"], ctx["mask"], ctx["rows"],
+                                                              ctx["gpu_out"], ctx["gpu_lse"])
+        log(f"[bench] oracle {result['cpu_baseline']['seconds']} s (prep {result['cpu_baseline']['prep_seconds']} s), "
+            f"parity {result['parity']}")
+    if share is not None:
+        if not args.no_cpu_baseline:
+            log(f"[bench] timing the oracle on the whole 32-way-share step ...")
+            share["cpu_baseline"], share["parity"] = oracle_leg(ws, sctx["X"], sctx["Xp"], sctx["mask"], sctx["rows"],
+                                                                sctx["gpu_out"], sctx["gpu_lse"])
+            log(f"[bench] oracle {share['cpu_baseline']['seconds']} s (prep {share['cpu_baseline']['prep_seconds']} s), "
+                f"parity {share['parity']}")
+        result["share32"] = share
     print(json.dumps(result), flush=True)
     return 0
 

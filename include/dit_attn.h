@@ -30,7 +30,9 @@
  *       q            [B, S_q, H, D]  bf16      (RoPE already applied)
  *       k, v         [B, S_kv, H, D] bf16
  *       cache_o      [P, B, S_q, H, D] bf16    state cache: output of each partition
- *       cache_lse    [P, B, H, S_q] f32        state cache: natural-log lse of each partition
+ *       cache_lse    [P, B, S_q, H] f32        state cache: natural-log lse of each partition
+ *                                              (each plane in the row order of out: a run of
+ *                                              row-heads reads one contiguous range)
  *       out          [B, S_q, H, D] bf16       merged output
  *       lse          [B, H, S_q] f32           merged lse
  *     All device buffers must be 16-byte aligned.
@@ -86,8 +88,11 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char *dit_status_string(int status);
 
-/* Bytes of device workspace dit_attn_partitioned needs for these sizes (for the
- * local-change partial sums).  Returns 0 if the sizes are invalid. */
+/* Bytes of device workspace dit_attn_partitioned needs for these sizes, for any split into
+ * n_qb query blocks: 256 bytes of schedule counters of the attention launch, the
+ * local-change partial sums of the attention kernel, then the importance partials of the
+ * merge (P floats per merge workgroup).  The split calls take the same workspace.  Returns
+ * 0 if the sizes are invalid. */
 size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P);
 
 /*
@@ -104,8 +109,13 @@ size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P);
  *   delta_out          device [B, n_qb] f32 or NULL: delta_i of the local states against the
  *                      states the local slots held before this call.  Needs local_part and
  *                      a workspace; with cache_valid given the local slots must be valid.
- *   workspace          device, >= dit_attn_workspace_bytes(...) when delta_out is given,
- *                      else may be NULL.  Contents on entry are ignored.
+ *   workspace          device, >= dit_attn_workspace_bytes(...) when delta_out or
+ *                      importance_out is given, else may be NULL.  Contents on entry are
+ *                      ignored.  When given, the attention launch is balanced across the
+ *                      XCDs (see dit_partition_attention), and the importance is computed
+ *                      inside the merge (partial sums per merge workgroup, finished in a
+ *                      fixed order).  Calls that share a workspace must not run at the same
+ *                      time.
  */
 int dit_attn_partitioned(const void *q, const void *k, const void *v,
                          int B, int S_q, int S_kv, int H, int D,
@@ -130,12 +140,16 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v,
  * memory, held until the process ends; its address is looked up once per device, on the
  * first call that needs it with that device current).  The call allocates nothing: no
  * hipMalloc, hipFree or allocating library routine.
- *   - delta_out given and dit_attn_workspace_bytes(...) > DIT_SCRATCH_BYTES:
- *     DIT_ERR_WORKSPACE (e.g. B = 1, H = 40 allows about 3,270 query tiles of 128 rows
- *     plus blocks, S_q up to ~410,000 rows).
- *   - The array keeps the last call's contents; every entry a call reads is written by the
- *     same call, so nothing needs clearing.  Calls that overlap on one GPU (on different
- *     streams, or from different threads) share the array and race: serialise them.
+ *   - delta_out given and 256 + B * (ceil(S_q / 128) + n_qb) * H * 8 bytes (the schedule
+ *     counters and the local-change partials) above DIT_SCRATCH_BYTES: DIT_ERR_WORKSPACE
+ *     (e.g. B = 1, H = 40 allows about 3,270 query tiles of 128 rows plus blocks, S_q up to
+ *     ~410,000 rows).
+ *   - The array holds the attention launch's schedule counters (cleared by each call with a
+ *     small kernel, not a memset) and the local-change partial sums; the importance, when
+ *     asked for, is taken in a second pass over the stored lse planes (no partials kept).
+ *     The array keeps the last call's contents; every other entry a call reads is written by
+ *     the same call.  Calls that overlap on one GPU (on different streams, or from different
+ *     threads) share the array and race: serialise them.
  *   - Unlike the other calls this one keeps state across calls (the per-device address).
  */
 int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v,
@@ -160,14 +174,19 @@ int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v,
  *   cache_valid        host [n_qb * P] or NULL, as for dit_attn_partitioned: when given, a
  *                      slot that is neither recomputed nor marked valid is
  *                      DIT_ERR_CACHE_INVALID (a merge of the cache after this call would
- *                      read it), and so is a local slot marked invalid when delta_partials
- *                      is given.
- *   delta_partials     device or NULL.  When given (with local_part), the kernel also writes,
- *                      per (query tile, head) of each block's local partition, the sums
- *                      sum (O_new - O_old)^2 and sum O_old^2 over the tile's rows and D,
- *                      where O_old is the slot's content before this call and O_new the bf16
- *                      value written.  Layout and size are internal: pass the workspace of
- *                      dit_attn_workspace_bytes and finish with dit_local_change_finalize.
+ *                      read it), and so is a local slot marked invalid when the local-change
+ *                      partials are written.
+ *   workspace          device or NULL, of workspace_bytes >= dit_attn_workspace_bytes(...).
+ *                      When given, the launch is balanced across the XCDs (the first 256
+ *                      bytes hold the counters through which workgroups claim the last fifth
+ *                      of each XCD's items; they are cleared by the call itself); without
+ *                      it every workgroup's item is fixed at launch.  When given together
+ *                      with local_part, the kernel also writes, per (query tile, head) of
+ *                      each block's local partition, the sums sum (O_new - O_old)^2 and
+ *                      sum O_old^2 over the tile's rows and D, where O_old is the slot's
+ *                      content before this call and O_new the value written; finish them
+ *                      with dit_local_change_finalize on the same workspace.  Calls that
+ *                      share a workspace must not run at the same time.
  */
 int dit_partition_attention(const void *q, const void *k, const void *v,
                             int B, int S_q, int S_kv, int H, int D,
@@ -178,7 +197,7 @@ int dit_partition_attention(const void *q, const void *k, const void *v,
                             const uint8_t *cache_valid,
                             void *cache_o, float *cache_lse,
                             float softmax_scale,
-                            void *delta_partials, size_t workspace_bytes,
+                            void *workspace, size_t workspace_bytes,
                             void *stream);
 
 /*
@@ -186,10 +205,19 @@ int dit_partition_attention(const void *q, const void *k, const void *v,
  * as the partition-attention call left them) into out / lse by LSE-weighted combination in
  * fp32; states with lse = -inf carry no weight; if every state is empty, out = 0 and
  * lse = -inf.
+ *   importance_out     device [B, n_qb, P] f32 or NULL (anchor steps): the partition
+ *                      importance of dit_importance, computed in the same pass from the merge
+ *                      weights (per-workgroup partial sums in the workspace, then a
+ *                      fixed-order reduction per block and partition).  Needs q_offsets
+ *                      [n_qb + 1] and the workspace of dit_attn_workspace_bytes; when
+ *                      importance_out is NULL they are ignored and may be NULL.
  */
 int dit_state_merge(const void *cache_o, const float *cache_lse,
                     int B, int S_q, int H, int D, int P,
                     void *out, float *lse,
+                    const int32_t *q_offsets, int n_qb,
+                    float *importance_out,
+                    void *workspace, size_t workspace_bytes,
                     void *stream);
 
 /*
@@ -199,14 +227,15 @@ int dit_state_merge(const void *cache_o, const float *cache_lse,
  * e4m3 codes plus one f32 scale per (partition, batch, head, row):
  *   cache_q8     [P, B, S_q, H, D] u8    code c of element x: the e4m3 value nearest
  *                                        x / s (round to nearest, ties to even)
- *   cache_scale  [P, B, H, S_q] f32      s = max_d |O_p| / 448 over the row-head's D values
+ *   cache_scale  [P, B, S_q, H] f32      s = max_d |O_p| / 448 over the row-head's D values
  *                                        (0 for an all-zero state: codes 0)
  *   cache_lse    as for the bf16 cache
  * The slot's value is s * e4m3(c); per element it is within max(2^-4 |x|, 2^-10 s) of the
  * fp32 state.  Per row-head and plane the cache holds D + 8 bytes instead of 2 D + 4.
- * delta_partials of dit_partition_attention_fp8 compare the dequantized new and old slot
+ * The local-change partials of dit_partition_attention_fp8 compare the dequantized new and old slot
  * values.  dit_state_merge_fp8 folds each plane's scale into its merge weight,
- * out = sum_p s_p e^{lse_p - lse} e4m3(c_p), accumulated in fp32, written as bf16.
+ * out = sum_p s_p e^{lse_p - lse} e4m3(c_p), accumulated in fp32, written as bf16; its
+ * importance arguments are those of dit_state_merge (the weights without the scales).
  * Argument checks and errors as for the bf16 calls (cache_valid included: reuse of a slot
  * marked never computed is DIT_ERR_CACHE_INVALID); cache_scale must be non-NULL.
  * dit_state_merge_fp8 reads every slot: call it only after a dit_partition_attention_fp8
@@ -221,12 +250,15 @@ int dit_partition_attention_fp8(const void *q, const void *k, const void *v,
                                 const uint8_t *cache_valid,
                                 void *cache_q8, float *cache_scale, float *cache_lse,
                                 float softmax_scale,
-                                void *delta_partials, size_t workspace_bytes,
+                                void *workspace, size_t workspace_bytes,
                                 void *stream);
 
 int dit_state_merge_fp8(const void *cache_q8, const float *cache_scale, const float *cache_lse,
                         int B, int S_q, int H, int D, int P,
                         void *out, float *lse,
+                        const int32_t *q_offsets, int n_qb,
+                        float *importance_out,
+                        void *workspace, size_t workspace_bytes,
                         void *stream);
 
 /*
@@ -253,9 +285,9 @@ int dit_state_merge_masked(const void *cache_o, const float *cache_lse,
  * states of runs of adjacent partitions into coarser states, with no recomputation.
  * Output plane g is the LSE-weighted combination of input planes
  * group_offsets[g] .. group_offsets[g+1]-1 (same rule as dit_state_merge, fp32 math).
- *   cache_o, cache_lse   device in: [P_in, B, S_q, H, D] bf16, [P_in, B, H, S_q] f32
+ *   cache_o, cache_lse   device in: [P_in, B, S_q, H, D] bf16, [P_in, B, S_q, H] f32
  *   group_offsets        host [G+1]: 0 = first, strictly increasing, last = P_in
- *   out_o, out_lse       device out: [G, B, S_q, H, D] bf16, [G, B, H, S_q] f32; must not
+ *   out_o, out_lse       device out: [G, B, S_q, H, D] bf16, [G, B, S_q, H] f32; must not
  *                        overlap the input planes
  * Applying it again to its output coarsens further (composition is associative).  After
  * composing, later steps run with the group offsets as partition offsets and the composed
@@ -270,7 +302,9 @@ int dit_state_compose(const void *cache_o, const float *cache_lse, int P_in,
 /*
  * Partition importance from the cached states and the merged lse of this step:
  * importance_out[b, i, p] = mean over rows r of block i and heads h of
- * e^{cache_lse[p, b, h, r] - lse[b, h, r]}  (0 for empty partitions).
+ * e^{cache_lse[p, b, r, h] - lse[b, h, r]}  (0 for empty partitions).  A second pass over the
+ * stored lse planes; it needs no workspace (dit_state_merge computes the same inside the
+ * merge).
  */
 int dit_importance(const float *cache_lse, const float *lse,
                    int B, int S_q, int H, int P,
@@ -279,11 +313,11 @@ int dit_importance(const float *cache_lse, const float *lse,
                    void *stream);
 
 /*
- * Finish the local-change reduction started by dit_partition_attention:
- * delta_out[b, i] = sqrt(sum (O_new - O_old)^2) / sqrt(sum O_old^2) over block i's rows,
- * heads and D (NaN if the old state is all zero).
+ * Finish the local-change reduction started by dit_partition_attention (the partials in its
+ * workspace): delta_out[b, i] = sqrt(sum (O_new - O_old)^2) / sqrt(sum O_old^2) over block
+ * i's rows, heads and D (NaN if the old state is all zero).
  */
-int dit_local_change_finalize(const void *delta_partials, size_t workspace_bytes,
+int dit_local_change_finalize(const void *workspace, size_t workspace_bytes,
                               int B, int S_q, int H, int D,
                               const int32_t *q_offsets, int n_qb,
                               float *delta_out,

@@ -37,9 +37,9 @@ SIGNATURES = {
                                             P_i32, c_int, P_i32, c_int, P_i32, P_u8, P_u8,
                                             c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p]),
     "dit_state_merge_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
-                                    c_void_p, c_void_p, c_void_p]),
+                                    c_void_p, c_void_p, P_i32, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "dit_state_merge": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
-                                c_void_p, c_void_p, c_void_p]),
+                                c_void_p, c_void_p, P_i32, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "dit_state_merge_masked": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, P_i32, c_int, P_u8,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dit_state_compose": (c_int, [c_void_p, c_void_p, c_int, P_i32, c_int, c_int, c_int, c_int, c_int,

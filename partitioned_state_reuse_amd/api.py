@@ -109,7 +109,7 @@ def attn_partitioned(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_l
         _i32(q_offsets), n_qb, _i32(kv_offsets), P,
         None if local_part is None else _i32(local_part), _u8(recompute),
         None if cache_valid is None else _u8(cache_valid),
-        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"),
+        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"),
         _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), float(scale),
         _dev(importance_out, F32, (B, n_qb, P), "importance_out"), _dev(delta_out, F32, (B, n_qb), "delta_out"),
         wp, ws_bytes, _stream(stream)))
@@ -127,55 +127,77 @@ def attn_partitioned_noalloc(q, k, v, q_offsets, kv_offsets, recompute, cache_o,
         _i32(q_offsets), n_qb, _i32(kv_offsets), P,
         None if local_part is None else _i32(local_part), _u8(recompute),
         None if cache_valid is None else _u8(cache_valid),
-        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"),
+        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"),
         _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), float(scale),
         _dev(importance_out, F32, (B, n_qb, P), "importance_out"), _dev(delta_out, F32, (B, n_qb), "delta_out"),
         _stream(stream)))
 
 
 def partition_attention(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, *,
-                        local_part=None, cache_valid=None, scale: float = 0.0, delta_partials=None,
+                        local_part=None, cache_valid=None, scale: float = 0.0, workspace=None,
                         stream=None) -> None:
+    """dit_partition_attention.  With a workspace the launch is balanced across the XCDs; with
+    local_part as well it also writes the local-change partial sums (finish them with
+    local_change_finalize)."""
     (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
     n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
-    wp, ws_bytes = _ws(delta_partials, "delta_partials")
+    wp, ws_bytes = _ws(workspace, "workspace")
     _check(_lib.lib().dit_partition_attention(
         qp, kp, vp, B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
         None if local_part is None else _i32(local_part), _u8(recompute),
         None if cache_valid is None else _u8(cache_valid),
-        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"),
+        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"),
         float(scale), wp, ws_bytes, _stream(stream)))
 
 
 def partition_attention_fp8(q, k, v, q_offsets, kv_offsets, recompute, cache_q8, cache_scale, cache_lse, *,
-                            local_part=None, cache_valid=None, scale: float = 0.0, delta_partials=None,
+                            local_part=None, cache_valid=None, scale: float = 0.0, workspace=None,
                             stream=None) -> None:
     """partition_attention into the compressed cache (cache_q8 uint8 e4m3 codes,
-    cache_scale one f32 scale per partition, batch, head and row)."""
+    cache_scale one f32 scale per partition, batch, row and head)."""
     (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
     n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
-    wp, ws_bytes = _ws(delta_partials, "delta_partials")
+    wp, ws_bytes = _ws(workspace, "workspace")
     _check(_lib.lib().dit_partition_attention_fp8(
         qp, kp, vp, B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
         None if local_part is None else _i32(local_part), _u8(recompute),
         None if cache_valid is None else _u8(cache_valid),
-        _dev(cache_q8, U8, (P, B, S_q, H, D), "cache_q8"), _dev(cache_scale, F32, (P, B, H, S_q), "cache_scale"),
-        _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), float(scale), wp, ws_bytes, _stream(stream)))
+        _dev(cache_q8, U8, (P, B, S_q, H, D), "cache_q8"), _dev(cache_scale, F32, (P, B, S_q, H), "cache_scale"),
+        _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"), float(scale), wp, ws_bytes, _stream(stream)))
 
 
-def state_merge_fp8(cache_q8, cache_scale, cache_lse, out, lse, *, stream=None) -> None:
+def _imp_args(q_offsets, importance_out, workspace, B, P):
+    """q_offsets, n_qb, importance address, workspace address and bytes of a merge."""
+    if importance_out is None:
+        return None, 0, None, None, 0
+    n_qb = len(q_offsets) - 1
+    wp, ws_bytes = _ws(workspace, "workspace")
+    return _i32(q_offsets), n_qb, _dev(importance_out, F32, (B, n_qb, P), "importance_out"), wp, ws_bytes
+
+
+def state_merge_fp8(cache_q8, cache_scale, cache_lse, out, lse, *, q_offsets=None, importance_out=None,
+                    workspace=None, stream=None) -> None:
+    """Merge of the compressed cache; with importance_out (and q_offsets, workspace) also the
+    partition importance in the same pass."""
     P, B, S_q, H, D = cache_q8.shape
+    qo, n_qb, ip, wp, ws_bytes = _imp_args(q_offsets, importance_out, workspace, B, P)
     _check(_lib.lib().dit_state_merge_fp8(
-        _dev(cache_q8, U8, None, "cache_q8"), _dev(cache_scale, F32, (P, B, H, S_q), "cache_scale"),
-        _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), B, S_q, H, D, P,
-        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), _stream(stream)))
+        _dev(cache_q8, U8, None, "cache_q8"), _dev(cache_scale, F32, (P, B, S_q, H), "cache_scale"),
+        _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"), B, S_q, H, D, P,
+        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), qo, n_qb, ip, wp, ws_bytes,
+        _stream(stream)))
 
 
-def state_merge(cache_o, cache_lse, out, lse, *, stream=None) -> None:
+def state_merge(cache_o, cache_lse, out, lse, *, q_offsets=None, importance_out=None, workspace=None,
+                stream=None) -> None:
+    """Merge of the P cached states; with importance_out (and q_offsets, workspace) also the
+    partition importance in the same pass."""
     P, B, S_q, H, D = cache_o.shape
+    qo, n_qb, ip, wp, ws_bytes = _imp_args(q_offsets, importance_out, workspace, B, P)
     _check(_lib.lib().dit_state_merge(
-        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), B, S_q, H, D, P,
-        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), _stream(stream)))
+        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"), B, S_q, H, D, P,
+        _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), qo, n_qb, ip, wp, ws_bytes,
+        _stream(stream)))
 
 
 def state_merge_masked(cache_o, cache_lse, q_offsets, plane_select, out, lse, *, extra_o=None, extra_lse=None,
@@ -183,7 +205,7 @@ def state_merge_masked(cache_o, cache_lse, q_offsets, plane_select, out, lse, *,
     """Merge, per query block, only the selected cache planes (plus an optional extra state)."""
     P, B, S_q, H, D = cache_o.shape
     _check(_lib.lib().dit_state_merge_masked(
-        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), B, S_q, H, D, P,
+        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"), B, S_q, H, D, P,
         _i32(q_offsets), len(q_offsets) - 1, _u8(plane_select),
         _dev(extra_o, BF16, (B, S_q, H, D), "extra_o"), _dev(extra_lse, F32, (B, H, S_q), "extra_lse"),
         _dev(out, BF16, (B, S_q, H, D), "out"), _dev(lse, F32, (B, H, S_q), "lse"), _stream(stream)))
@@ -194,22 +216,22 @@ def state_compose(cache_o, cache_lse, group_offsets, out_o, out_lse, *, stream=N
     P, B, S_q, H, D = cache_o.shape
     G = len(group_offsets) - 1
     _check(_lib.lib().dit_state_compose(
-        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, H, S_q), "cache_lse"), P,
+        _dev(cache_o, BF16, None, "cache_o"), _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"), P,
         _i32(group_offsets), G, B, S_q, H, D,
-        _dev(out_o, BF16, (G, B, S_q, H, D), "out_o"), _dev(out_lse, F32, (G, B, H, S_q), "out_lse"),
+        _dev(out_o, BF16, (G, B, S_q, H, D), "out_o"), _dev(out_lse, F32, (G, B, S_q, H), "out_lse"),
         _stream(stream)))
 
 
 def importance(cache_lse, lse, q_offsets, importance_out, *, stream=None) -> None:
-    P, B, H, S_q = cache_lse.shape
+    P, B, S_q, H = cache_lse.shape
     n_qb = len(q_offsets) - 1
     _check(_lib.lib().dit_importance(
         _dev(cache_lse, F32, None, "cache_lse"), _dev(lse, F32, (B, H, S_q), "lse"), B, S_q, H, P,
         _i32(q_offsets), n_qb, _dev(importance_out, F32, (B, n_qb, P), "importance_out"), _stream(stream)))
 
 
-def local_change_finalize(delta_partials, B, S_q, H, D, q_offsets, delta_out, *, stream=None) -> None:
-    wp, ws_bytes = _ws(delta_partials, "delta_partials")
+def local_change_finalize(workspace, B, S_q, H, D, q_offsets, delta_out, *, stream=None) -> None:
+    wp, ws_bytes = _ws(workspace, "workspace")
     n_qb = len(q_offsets) - 1
     _check(_lib.lib().dit_local_change_finalize(wp, ws_bytes, B, S_q, H, D, _i32(q_offsets), n_qb,
                                                 _dev(delta_out, F32, (B, n_qb), "delta_out"), _stream(stream)))
@@ -279,11 +301,11 @@ class SelectiveAttention:
         self.cache_format = cache_format
         if cache_format == "fp8":
             self.cache_o = torch.empty((self.P, B, S_q, H, D), dtype=torch.uint8, device=device)
-            self.cache_scale = torch.empty((self.P, B, H, S_q), dtype=torch.float32, device=device)
+            self.cache_scale = torch.empty((self.P, B, S_q, H), dtype=torch.float32, device=device)
         else:
             self.cache_o = torch.empty((self.P, B, S_q, H, D), dtype=torch.bfloat16, device=device)
             self.cache_scale = None
-        self.cache_lse = torch.empty((self.P, B, H, S_q), dtype=torch.float32, device=device)
+        self.cache_lse = torch.empty((self.P, B, S_q, H), dtype=torch.float32, device=device)
         self.out = torch.empty((B, S_q, H, D), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((B, H, S_q), dtype=torch.float32, device=device)
         self.importance = torch.empty((B, self.n_qb, self.P), dtype=torch.float32, device=device)
@@ -314,8 +336,8 @@ class SelectiveAttention:
                            self.partial_lse, stream=side_stream)
         do_delta = want_delta and all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
         partition_attention(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
-                            local_part=self.local_part, cache_valid=self.valid, scale=scale,
-                            delta_partials=self.workspace if do_delta else None, stream=main)
+                            local_part=self.local_part if do_delta else None, cache_valid=self.valid, scale=scale,
+                            workspace=self.workspace, stream=main)
         done = torch.cuda.Event()
         done.record(side_stream)
         main.wait_event(done)
@@ -343,12 +365,12 @@ class SelectiveAttention:
         out.cache_format, out.cache_scale = "bf16", None
         dev = self.cache_o.device
         out.cache_o = torch.empty((out.P, self.B, self.S_q, self.H, self.D), dtype=torch.bfloat16, device=dev)
-        out.cache_lse = torch.empty((out.P, self.B, self.H, self.S_q), dtype=torch.float32, device=dev)
+        out.cache_lse = torch.empty((out.P, self.B, self.S_q, self.H), dtype=torch.float32, device=dev)
         state_compose(self.cache_o, self.cache_lse, go, out.cache_o, out.cache_lse, stream=stream)
         out.out, out.lse = self.out, self.lse
         out.importance = torch.empty((self.B, out.n_qb, out.P), dtype=torch.float32, device=dev)
         out.delta = self.delta
-        out.workspace = self.workspace
+        out.workspace = self.workspace     # fewer partitions: the workspace bound only shrinks
         out.valid = np.stack([self.valid[:, go[j]:go[j + 1]].all(axis=1) for j in range(out.P)], axis=1).astype(np.uint8)
         return out
 
@@ -362,12 +384,11 @@ class SelectiveAttention:
         do_delta = want_delta and local_valid
         if self.cache_format == "fp8":
             partition_attention_fp8(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o,
-                                    self.cache_scale, self.cache_lse, local_part=self.local_part,
-                                    cache_valid=self.valid, scale=scale,
-                                    delta_partials=self.workspace if do_delta else None, stream=stream)
-            state_merge_fp8(self.cache_o, self.cache_scale, self.cache_lse, self.out, self.lse, stream=stream)
-            if want_importance:
-                importance(self.cache_lse, self.lse, self.q_offsets, self.importance, stream=stream)
+                                    self.cache_scale, self.cache_lse, local_part=self.local_part if do_delta else None,
+                                    cache_valid=self.valid, scale=scale, workspace=self.workspace, stream=stream)
+            state_merge_fp8(self.cache_o, self.cache_scale, self.cache_lse, self.out, self.lse,
+                            q_offsets=self.q_offsets, importance_out=self.importance if want_importance else None,
+                            workspace=self.workspace, stream=stream)
             if do_delta:
                 local_change_finalize(self.workspace, self.B, self.S_q, self.H, self.D, self.q_offsets, self.delta,
                                       stream=stream)
@@ -376,7 +397,6 @@ class SelectiveAttention:
         attn_partitioned(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
                          self.out, self.lse, local_part=self.local_part, cache_valid=self.valid, scale=scale,
                          importance_out=self.importance if want_importance else None,
-                         delta_out=self.delta if do_delta else None,
-                         workspace=self.workspace if do_delta else None, stream=stream)
+                         delta_out=self.delta if do_delta else None, workspace=self.workspace, stream=stream)
         self.valid |= recompute
         return do_delta

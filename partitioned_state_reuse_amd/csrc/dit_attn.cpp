@@ -63,10 +63,44 @@ void fill_blocks(BlockDesc &bd, const int32_t *q_offsets, int n_qb) {
   bd.n_tiles = bd.tile_prefix[n_qb];
 }
 
+// Workspace layout: the attention launch's schedule counters (kSchedBytes), the local-change
+// partial sums of the attention kernel, then (from the next 256-byte boundary) the
+// importance partials of the merge.
 size_t delta_ws_bytes(int B, int S_q, int H, int n_qb) {
   // upper bound on the tile count of any split into n_qb blocks
   const int64_t tiles = (int64_t)(S_q + dit::kBlockM - 1) / dit::kBlockM + n_qb;
   return (size_t)B * (size_t)tiles * (size_t)H * 2 * sizeof(float);
+}
+
+constexpr size_t kDeltaOffset = dit::kSchedBytes;
+
+size_t imp_ws_offset(int B, int S_q, int H, int n_qb) {
+  return (kDeltaOffset + delta_ws_bytes(B, S_q, H, n_qb) + 255) & ~(size_t)255;
+}
+
+float *delta_region(void *workspace) { return (float *)((char *)workspace + kDeltaOffset); }
+
+// Upper bound on the importance partials of any split into n_qb blocks: every merge variant
+// takes at least 16 row-heads per workgroup, and each block adds at most one partly filled
+// workgroup.
+size_t imp_ws_bound(int B, int S_q, int H, int n_qb, int P) {
+  const int64_t wgs = ((int64_t)S_q * H + 15) / 16 + n_qb;
+  return (size_t)B * (size_t)wgs * (size_t)P * sizeof(float);
+}
+
+// Validate an importance request of a merge and return the partials' address in the workspace.
+int check_importance(int D, bool fp8, int B, int S_q, int H, int P, const int32_t *q_offsets, int n_qb,
+                     void *workspace, size_t workspace_bytes, BlockDesc &bd, float *&imp_part) {
+  int st = check_q_offsets(q_offsets, n_qb, S_q);
+  if (st) return st;
+  fill_blocks(bd, q_offsets, n_qb);
+  const int64_t nwg = dit::merge_workgroups(D, fp8, &bd, B, S_q, H);
+  if (nwg * 256 > (int64_t)UINT32_MAX) return DIT_ERR_SHAPE;
+  if (!workspace) return DIT_ERR_WORKSPACE;
+  const size_t off = imp_ws_offset(B, S_q, H, n_qb);
+  if (workspace_bytes < off + (size_t)nwg * (size_t)P * sizeof(float)) return DIT_ERR_WORKSPACE;
+  imp_part = (float *)((char *)workspace + off);
+  return DIT_OK;
 }
 
 // Validate and build the work description of one partition-attention launch.
@@ -94,10 +128,11 @@ int build_attn(const void *q, const void *k, const void *v, int B, int S_q, int 
     for (int e = 0; e < n_qb * P; ++e)
       if (!recompute[e] && !cache_valid[e]) return DIT_ERR_CACHE_INVALID;
   }
+  if (workspace && workspace_bytes < dit::kSchedBytes) return DIT_ERR_WORKSPACE;
   if (want_delta) {
     if (!local_part) return DIT_ERR_NULL;
     if (!workspace) return DIT_ERR_WORKSPACE;
-    if (workspace_bytes < delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
+    if (workspace_bytes < kDeltaOffset + delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
     if (cache_valid)
       for (int i = 0; i < n_qb; ++i)
         if (!cache_valid[i * P + local_part[i]]) return DIT_ERR_CACHE_INVALID;
@@ -126,9 +161,11 @@ int build_attn(const void *q, const void *k, const void *v, int B, int S_q, int 
     desc.item_prefix[p + 1] = desc.item_prefix[p] + items;
   }
   desc.items_per_head = desc.item_prefix[P];
-  // one workgroup of kWaves * 64 threads per (batch, head, item); a dispatch counts its
-  // work-items in 32 bits
+  // one workgroup of kWaves * 64 threads per (batch, head, item), plus the spare workgroups
+  // of a balanced launch; a dispatch counts its work-items in 32 bits
   if ((int64_t)B * H * desc.items_per_head * (dit::kWaves * 64) > (int64_t)UINT32_MAX) return DIT_ERR_SHAPE;
+  if (dit::attention_launch_shape(desc, workspace != nullptr).workgroups * (dit::kWaves * 64) > (int64_t)UINT32_MAX)
+    return DIT_ERR_SHAPE;
   for (int i = 0; i < n_qb; ++i) desc.local_part[i] = (want_delta && local_part) ? local_part[i] : -1;
   return DIT_OK;
 }
@@ -138,12 +175,14 @@ float scale_log2_of(float softmax_scale, int D) {
   return s * 1.4426950408889634f;
 }
 
-// One selective step (dit_attn_partitioned) on a given workspace.
+// One selective step (dit_attn_partitioned) on a given workspace.  fused_importance: the
+// importance comes from the merge's partials (in the workspace); otherwise from a second
+// pass over the stored lse planes, which needs no workspace.
 int run_partitioned(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H, int D,
                     const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P, const int32_t *local_part,
                     const uint8_t *recompute, const uint8_t *cache_valid, void *cache_o, float *cache_lse, void *out,
                     float *lse, float softmax_scale, float *importance_out, float *delta_out, void *workspace,
-                    size_t workspace_bytes, void *stream) {
+                    size_t workspace_bytes, bool fused_importance, void *stream) {
   try {
     if (!out || !lse) return DIT_ERR_NULL;
     AttnDesc desc;
@@ -151,18 +190,25 @@ int run_partitioned(const void *q, const void *k, const void *v, int B, int S_q,
     int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
                         cache_valid, cache_o, cache_lse, want_delta, workspace, workspace_bytes, desc);
     if (st) return st;
-    hipStream_t s = as_stream(stream);
-    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse, want_delta ? (float *)workspace : nullptr,
-                                        desc, scale_log2_of(softmax_scale, D), s) != hipSuccess)
-      return DIT_ERR_HIP;
-    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, s) != hipSuccess)
-      return DIT_ERR_HIP;
     BlockDesc bd;
     fill_blocks(bd, q_offsets, n_qb);
-    if (importance_out &&
+    float *imp_part = nullptr;
+    const bool fuse = importance_out != nullptr && fused_importance;
+    if (fuse &&
+        (st = check_importance(D, false, B, S_q, H, P, q_offsets, n_qb, workspace, workspace_bytes, bd, imp_part)))
+      return st;
+    hipStream_t s = as_stream(stream);
+    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse,
+                                        want_delta ? delta_region(workspace) : nullptr, (int *)workspace, desc,
+                                        scale_log2_of(softmax_scale, D), s) != hipSuccess)
+      return DIT_ERR_HIP;
+    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, false, fuse ? &bd : nullptr, imp_part,
+                                importance_out, s) != hipSuccess)
+      return DIT_ERR_HIP;
+    if (importance_out && !fuse &&
         dit::launch_importance(cache_lse, lse, B, S_q, H, P, bd, importance_out, s) != hipSuccess)
       return DIT_ERR_HIP;
-    if (want_delta && dit::launch_delta_finalize((const float *)workspace, B, H, bd, delta_out, s) != hipSuccess)
+    if (want_delta && dit::launch_delta_finalize(delta_region(workspace), B, H, bd, delta_out, s) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
   } catch (...) {
@@ -193,23 +239,24 @@ const char *dit_status_string(int status) {
 size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P) {
   if (check_dims(B, S_q, 0, H, D) != DIT_OK) return 0;
   if (n_qb < 1 || n_qb > DIT_MAX_BLOCKS || P < 1 || P > DIT_MAX_PARTITIONS) return 0;
-  return delta_ws_bytes(B, S_q, H, n_qb);
+  return imp_ws_offset(B, S_q, H, n_qb) + imp_ws_bound(B, S_q, H, n_qb, P);
 }
 
 int dit_partition_attention(const void *q, const void *k, const void *v, int B, int S_q, int S_kv,
                             int H, int D, const int32_t *q_offsets, int n_qb,
                             const int32_t *kv_offsets, int P, const int32_t *local_part,
                             const uint8_t *recompute, const uint8_t *cache_valid, void *cache_o,
-                            float *cache_lse, float softmax_scale, void *delta_partials,
+                            float *cache_lse, float softmax_scale, void *workspace,
                             size_t workspace_bytes, void *stream) {
   try {
     AttnDesc desc;
-    const bool want_delta = delta_partials != nullptr;
+    const bool want_delta = workspace != nullptr && local_part != nullptr;
     int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part,
-                        recompute, cache_valid, cache_o, cache_lse, want_delta, delta_partials,
+                        recompute, cache_valid, cache_o, cache_lse, want_delta, workspace,
                         workspace_bytes, desc);
     if (st) return st;
-    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse, (float *)delta_partials, desc,
+    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse,
+                                        want_delta ? delta_region(workspace) : nullptr, (int *)workspace, desc,
                                         scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
@@ -222,16 +269,17 @@ int dit_partition_attention_fp8(const void *q, const void *k, const void *v, int
                                 const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P,
                                 const int32_t *local_part, const uint8_t *recompute, const uint8_t *cache_valid,
                                 void *cache_q8, float *cache_scale, float *cache_lse, float softmax_scale,
-                                void *delta_partials, size_t workspace_bytes, void *stream) {
+                                void *workspace, size_t workspace_bytes, void *stream) {
   try {
     if (!cache_scale) return DIT_ERR_NULL;
     AttnDesc desc;
-    const bool want_delta = delta_partials != nullptr;
+    const bool want_delta = workspace != nullptr && local_part != nullptr;
     int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
-                        cache_valid, cache_q8, cache_lse, want_delta, delta_partials, workspace_bytes, desc);
+                        cache_valid, cache_q8, cache_lse, want_delta, workspace, workspace_bytes, desc);
     if (st) return st;
-    if (dit::launch_partition_attention(D, true, q, k, v, cache_q8, cache_scale, cache_lse, (float *)delta_partials,
-                                        desc, scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
+    if (dit::launch_partition_attention(D, true, q, k, v, cache_q8, cache_scale, cache_lse,
+                                        want_delta ? delta_region(workspace) : nullptr, (int *)workspace, desc,
+                                        scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
   } catch (...) {
@@ -240,14 +288,21 @@ int dit_partition_attention_fp8(const void *q, const void *k, const void *v, int
 }
 
 int dit_state_merge_fp8(const void *cache_q8, const float *cache_scale, const float *cache_lse, int B, int S_q,
-                        int H, int D, int P, void *out, float *lse, void *stream) {
+                        int H, int D, int P, void *out, float *lse, const int32_t *q_offsets, int n_qb,
+                        float *importance_out, void *workspace, size_t workspace_bytes, void *stream) {
   try {
     if (!cache_q8 || !cache_scale || !cache_lse || !out || !lse) return DIT_ERR_NULL;
     int st = check_dims(B, S_q, 0, H, D);
     if (st) return st;
     if (P < 1 || P > DIT_MAX_PARTITIONS) return DIT_ERR_SHAPE;
-    if (dit::launch_state_merge_fp8(D, P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, as_stream(stream)) !=
-        hipSuccess)
+    BlockDesc bd;
+    float *imp_part = nullptr;
+    if (importance_out &&
+        (st = check_importance(D, true, B, S_q, H, P, q_offsets, n_qb, workspace, workspace_bytes, bd, imp_part)))
+      return st;
+    if (dit::launch_state_merge_fp8(D, P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H,
+                                    importance_out ? &bd : nullptr, imp_part, importance_out,
+                                    as_stream(stream)) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
   } catch (...) {
@@ -256,13 +311,21 @@ int dit_state_merge_fp8(const void *cache_q8, const float *cache_scale, const fl
 }
 
 int dit_state_merge(const void *cache_o, const float *cache_lse, int B, int S_q, int H, int D, int P,
-                    void *out, float *lse, void *stream) {
+                    void *out, float *lse, const int32_t *q_offsets, int n_qb, float *importance_out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
   try {
     if (!cache_o || !cache_lse || !out || !lse) return DIT_ERR_NULL;
     int st = check_dims(B, S_q, 0, H, D);
     if (st) return st;
     if (P < 1 || P > DIT_MAX_PARTITIONS) return DIT_ERR_SHAPE;
-    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, as_stream(stream)) != hipSuccess)
+    BlockDesc bd;
+    float *imp_part = nullptr;
+    if (importance_out &&
+        (st = check_importance(D, false, B, S_q, H, P, q_offsets, n_qb, workspace, workspace_bytes, bd, imp_part)))
+      return st;
+    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, false,
+                                importance_out ? &bd : nullptr, imp_part, importance_out,
+                                as_stream(stream)) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
   } catch (...) {
@@ -316,7 +379,8 @@ int dit_state_compose(const void *cache_o, const float *cache_lse, int P_in, con
     for (int g = 0; g < G; ++g) {
       const int a = group_offsets[g];
       if (dit::launch_state_merge(D, group_offsets[g + 1] - a, in_o + a * plane_o, cache_lse + a * plane_lse,
-                                  o + g * plane_o, out_lse + g * plane_lse, B, S_q, H, as_stream(stream)) != hipSuccess)
+                                  o + g * plane_o, out_lse + g * plane_lse, B, S_q, H, true, nullptr, nullptr,
+                                  nullptr, as_stream(stream)) != hipSuccess)
         return DIT_ERR_HIP;
     }
     return DIT_OK;
@@ -343,17 +407,17 @@ int dit_importance(const float *cache_lse, const float *lse, int B, int S_q, int
   }
 }
 
-int dit_local_change_finalize(const void *delta_partials, size_t workspace_bytes, int B, int S_q, int H,
+int dit_local_change_finalize(const void *workspace, size_t workspace_bytes, int B, int S_q, int H,
                               int D, const int32_t *q_offsets, int n_qb, float *delta_out, void *stream) {
   try {
-    if (!delta_partials || !delta_out) return DIT_ERR_NULL;
+    if (!workspace || !delta_out) return DIT_ERR_NULL;
     int st = check_dims(B, S_q, 0, H, D);
     if (st) return st;
     if ((st = check_q_offsets(q_offsets, n_qb, S_q))) return st;
-    if (workspace_bytes < delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
+    if (workspace_bytes < kDeltaOffset + delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
     BlockDesc bd;
     fill_blocks(bd, q_offsets, n_qb);
-    if (dit::launch_delta_finalize((const float *)delta_partials, B, H, bd, delta_out, as_stream(stream)) !=
+    if (dit::launch_delta_finalize(delta_region((void *)workspace), B, H, bd, delta_out, as_stream(stream)) !=
         hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
@@ -370,7 +434,7 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v, int B, int
                          void *stream) {
   return run_partitioned(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
                          cache_valid, cache_o, cache_lse, out, lse, softmax_scale, importance_out, delta_out,
-                         workspace, workspace_bytes, stream);
+                         workspace, workspace_bytes, true, stream);
 }
 
 int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H,
@@ -379,17 +443,15 @@ int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v, in
                                  void *cache_o, float *cache_lse, void *out, float *lse, float softmax_scale,
                                  float *importance_out, float *delta_out, void *stream) {
   try {
+    // the library's own device scratch stands in for the workspace: schedule counters and
+    // local-change partials (sizes beyond it are rejected by the workspace check,
+    // DIT_ERR_WORKSPACE); the importance is taken in a second pass, which needs none
     void *ws = nullptr;
-    size_t ws_bytes = 0;
-    if (delta_out != nullptr) {
-      // the library's own device scratch stands in for the workspace (sizes beyond it are
-      // rejected by the workspace check, DIT_ERR_WORKSPACE)
-      if (dit::scratch_address(&ws) != hipSuccess) return DIT_ERR_HIP;
-      ws_bytes = dit::kScratchBytes;
-    }
+    if (dit::scratch_address(&ws) != hipSuccess) return DIT_ERR_HIP;
+    const size_t ws_bytes = dit::kScratchBytes;
     return run_partitioned(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
                            cache_valid, cache_o, cache_lse, out, lse, softmax_scale, importance_out, delta_out, ws,
-                           ws_bytes, stream);
+                           ws_bytes, false, stream);
   } catch (...) {
     return DIT_ERR_INTERNAL;
   }

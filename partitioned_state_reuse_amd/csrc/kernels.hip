@@ -6,6 +6,7 @@
 // and "§1, Anchor-Guided Selection Planner"): per KV partition an attention state
 // (O_p, lse_p) is produced; the states are composed by LSE-weighted combination.
 #include <math.h>
+#include <string.h>
 
 #include <algorithm>
 #include <mutex>
@@ -147,7 +148,8 @@ template <int D, bool FP8>
 __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ k, const u16 *__restrict__ v,
     void *__restrict__ cache_o, float *__restrict__ cache_scale, float *__restrict__ cache_lse,
-    float *__restrict__ delta_part, const AttnDesc desc, const float scale_log2) {
+    float *__restrict__ delta_part, const AttnDesc desc, const float scale_log2, int *__restrict__ sched,
+    const int static_per) {
   using G = TileGeom<D>;
   constexpr int KK = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -168,12 +170,63 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- work item.  Workgroups are dealt round-robin to the 8 XCDs; remap so that
-  // consecutive items (same K/V partition) run on the same XCD and share its L2.
-  const int nwg = gridDim.x;
+  // ---- work item.  Workgroups are dealt round-robin to the 8 XCDs (workgroup w to XCD
+  // w mod 8); each XCD takes a contiguous range of the items, so that consecutive items (same
+  // K/V partition) run on one XCD and share its L2.  Without `sched` the k-th workgroup of
+  // an XCD takes the k-th item of its range.  With `sched`, the XCDs, which run at different
+  // clocks, are balanced: the first static_per items of each range are still taken that way,
+  // and the rest are claimed at run time through one counter per XCD (sched[0..7], zero at
+  // launch): a workgroup past the static part claims the next item of its own range, and
+  // once that is used up, the next item of another XCD's range.  The grid then holds
+  // spare workgroups per XCD, which exit when every item has been claimed.
   const int wg = blockIdx.x;
-  const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
-  const int item = xcd * per + min(xcd, rem) + (wg >> 3);
+  const int xcd = wg & 7;
+  const int n_items = desc.B * desc.H * desc.items_per_head;
+  int item;
+  {
+    const int per = n_items >> 3, rem = n_items & 7;
+    auto range_lo = [&](int x) { return x * per + min(x, rem); };
+    auto range_n = [&](int x) { return per + (x < rem ? 1 : 0); };
+    const int k = wg >> 3;
+    if (sched == nullptr) {
+      item = range_lo(xcd) + k;
+    } else if (k < min(static_per, range_n(xcd))) {
+      item = range_lo(xcd) + k;
+    } else {
+      // dynamic part of XCD x: items [lo + ns, lo + n), ns = min(static_per, n)
+      auto dyn_n = [&](int x) { return range_n(x) - min(static_per, range_n(x)); };
+      auto dyn_lo = [&](int x) { return range_lo(x) + min(static_per, range_n(x)); };
+      __shared__ int claimed;
+      if (wave == 0) {
+        int got = -1;
+        if (lane == 0) {
+          const int t = atomicAdd(&sched[xcd], 1);
+          if (t < dyn_n(xcd)) got = dyn_lo(xcd) + t;
+        }
+        got = __shfl(got, 0);
+        // Own range used up: look at every counter at once, claim from the first XCD after
+        // this one that has items left.  A failed claim leaves that counter past its range,
+        // so the loop ends after at most 8 failures.
+        while (got < 0) {
+          const bool left = lane < 8 && __hip_atomic_load(&sched[lane], __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT) < dyn_n(lane);
+          uint32_t m = (uint32_t)__ballot(left) & 0xffu;
+          if (m == 0) break;
+          m = ((m >> ((xcd + 1) & 7)) | (m << (8 - ((xcd + 1) & 7)))) & 0xffu;  // rotate: xcd + 1 first
+          const int y = (__builtin_ctz(m) + xcd + 1) & 7;
+          if (lane == 0) {
+            const int t = atomicAdd(&sched[y], 1);
+            if (t < dyn_n(y)) got = dyn_lo(y) + t;
+          }
+          got = __shfl(got, 0);
+        }
+        if (lane == 0) claimed = got;
+      }
+      __syncthreads();
+      item = claimed;
+      if (item < 0) return;  // every item has been claimed (uniform over the workgroup)
+    }
+  }
   const int per_head = desc.items_per_head;
   const int bh = item / per_head;
   int idx = item - bh * per_head;
@@ -490,8 +543,8 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   auto slot_of = [&](int r) {  // [P, B, S_q] index of query row r of this tile
     return ((int64_t)p * desc.B + b) * desc.S_q + q0 + r;
   };
-  auto lslot_of = [&](int r) {  // [P, B, H, S_q] index
-    return (((int64_t)p * desc.B + b) * H + head) * desc.S_q + q0 + r;
+  auto lslot_of = [&](int r) {  // [P, B, S_q, H] index
+    return slot_of(r) * H + head;
   };
   if constexpr (FP8) {
     // compressed slot: e4m3 codes of O / s with s = max_d |O| / 448 per (row, head); the
@@ -618,12 +671,10 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs (workgroup w runs on XCD w mod 8), and
-// each XCD has its own L2.  The merge kernels take row-heads in (row, head) order while
-// the lse (and scale) planes are [head][row], so one lse line serves the same heads of
-// several consecutive rows, i.e. a run of consecutive workgroups.  Remap so that each XCD
-// takes runs of `chunk` consecutive workgroups (each lse line is fetched into one L2),
-// while the 8 XCDs still stream neighbouring runs at the same time.  The ragged tail keeps
-// the identity mapping.
+// each XCD has its own L2.  Neighbouring merge workgroups share cache lines of the lse (and
+// scale) planes; remap so that each XCD takes runs of `chunk` consecutive workgroups (a
+// line is fetched into one L2), while the 8 XCDs still stream neighbouring runs at the same
+// time.  The ragged tail keeps the identity mapping.
 __device__ __forceinline__ int lse_chunked_item(int chunk) {
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int span = 8 * chunk;
@@ -637,39 +688,74 @@ __device__ __forceinline__ int lse_chunked_item(int chunk) {
 // H heads (RPW row-heads per workgroup).
 inline int merge_chunk(int RPW, int H) { return std::max(1, kMergeChunkRows * H / RPW); }
 
+// Placement of merge workgroups over row-heads rh = (b S_q + r) H + h.  Plain (n_qb = 0):
+// workgroup w takes RPW consecutive row-heads.  With importance partials, the workgroups of
+// each (batch, query block) cover only that block's row-heads, so that the partial sums of a
+// workgroup belong to one block: block i has ceil(|i| H / RPW) workgroups per batch,
+// wg_prefix counts them.
+struct MergeGrid {
+  int32_t n_qb;
+  int32_t wg_per_batch;
+  int32_t q_off[DIT_MAX_BLOCKS + 1];
+  int32_t wg_prefix[DIT_MAX_BLOCKS + 1];
+};
+
+template <int RPW>
+__device__ __forceinline__ void merge_rows(const MergeGrid &g, int w, int S_q, int H, int64_t total_rh,
+                                           int64_t &rh0, int64_t &rh_end) {
+  if (g.n_qb == 0) {
+    rh0 = (int64_t)w * RPW;
+    rh_end = total_rh;
+    return;
+  }
+  const int b = w / g.wg_per_batch;
+  const int wl = w - b * g.wg_per_batch;
+  int lo = 0, hi = g.n_qb - 1;  // last block i with wg_prefix[i] <= wl
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.wg_prefix[mid] <= wl) lo = mid; else hi = mid - 1;
+  }
+  rh0 = ((int64_t)b * S_q + g.q_off[lo]) * H + (int64_t)(wl - g.wg_prefix[lo]) * RPW;
+  rh_end = ((int64_t)b * S_q + g.q_off[lo + 1]) * H;
+}
+
 // ------------------------------------------------------------------------------------
 // State merge: one thread per 8 consecutive d of one (row, head), a workgroup per 16
 // consecutive row-heads (4 KB contiguous runs of every partition plane).  The row-head's
 // lanes first share out the merge weights (group_merge_weights: each lse value is loaded
 // by one lane, not by all of them), then the P bf16 states are streamed with 16-byte
 // non-temporal loads (PMAX >= P, unrolled) and combined in fp32; the merged output is
-// written with non-temporal stores (it is not re-read by this step).
+// written with non-temporal stores (it is not re-read by this step).  The cache's lse
+// planes are [row][head], like the rows of the output: a workgroup's lse values of one
+// plane are one contiguous run.
 // ------------------------------------------------------------------------------------
 // Merge weights of one row-head, computed by the TPR lanes that share it (one wave holds
 // whole groups): lane c loads the lse (and, with SCALED, the scale) of planes c, c + TPR,
-// ... only; the maximum and the sum of exponentials are reduced over the group with an xor
-// butterfly (every lane ends with the same values, in a fixed order); the weights
-// w_p = e^{lse_p - lse} (times s_p) go to wts[0 .. PMAX) in LDS, where every lane of the
-// group reads them.  Planes at or past P, planes outside the mask `pm` and empty states get
-// weight 0.  An extra state (extra_lse non-null, lse loaded by lane 0) takes part in the
-// merge with its weight in wts[PMAX].  Returns the merged lse (-inf when every state is
-// empty).
+// ... only, at index ci of each plane; the maximum and the sum of exponentials are reduced
+// over the group with an xor butterfly (every lane ends with the same values, in a fixed
+// order); the weights w_p = e^{lse_p - lse} (times s_p) go to wts[0 .. PMAX) in LDS, where
+// every lane of the group reads them, and, when `wraw` is given, the weights without the
+// scale to wraw.  Planes at or past P, planes outside the mask `pm`, empty states and row-heads
+// that are not `valid` (no loads at all) get weight 0.  An extra state (extra_lse non-null,
+// its lse at index xi loaded by lane 0) takes part in the merge with its weight in
+// wts[PMAX].  Returns the merged lse (-inf when every state is empty).
 template <int TPR, int PMAX, bool SCALED>
 __device__ __forceinline__ float group_merge_weights(const float *__restrict__ cache_lse,
-                                                     const float *__restrict__ cache_scale, int64_t li,
-                                                     int64_t plane_lse, int P, int c, float *wts,
-                                                     uint64_t pm = ~0ull,
-                                                     const float *__restrict__ extra_lse = nullptr) {
+                                                     const float *__restrict__ cache_scale, int64_t ci,
+                                                     int64_t plane_lse, int P, int c, bool valid, float *wts,
+                                                     float *wraw, uint64_t pm = ~0ull,
+                                                     const float *__restrict__ extra_lse = nullptr,
+                                                     int64_t xi = 0) {
   constexpr int NPL = (PMAX + TPR - 1) / TPR;
   float lv[NPL];
   float M = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
     const int p = c + TPR * k;
-    lv[k] = (p < P && ((pm >> p) & 1)) ? cache_lse[p * plane_lse + li] : -INFINITY;
+    lv[k] = (valid && p < P && ((pm >> p) & 1)) ? cache_lse[p * plane_lse + ci] : -INFINITY;
     M = fmaxf(M, lv[k]);
   }
-  const float lx = (extra_lse != nullptr && c == 0) ? extra_lse[li] : -INFINITY;
+  const float lx = (valid && extra_lse != nullptr && c == 0) ? extra_lse[xi] : -INFINITY;
   M = fmaxf(M, lx);
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -684,7 +770,8 @@ __device__ __forceinline__ float group_merge_weights(const float *__restrict__ c
     const int p = c + TPR * k;
     if (p < PMAX) {
       float w = (lv[k] > -INFINITY) ? __expf(lv[k] - L) : 0.f;
-      if constexpr (SCALED) w = (p < P) ? w * cache_scale[p * plane_lse + li] : 0.f;
+      if (wraw != nullptr) wraw[p] = w;
+      if constexpr (SCALED) w = (lv[k] > -INFINITY) ? w * cache_scale[p * plane_lse + ci] : 0.f;
       wts[p] = w;
     }
   }
@@ -697,146 +784,161 @@ __device__ __forceinline__ float group_merge_weights(const float *__restrict__ c
   return L;
 }
 
-template <int D, int PMAX>
+// Importance partials of one merge workgroup: thread p < P sums plane p's unscaled weights
+// over the workgroup's row-heads in order (rows that are not valid hold 0) and stores the sum
+// at imp_part[p * gridDim.x + w], plane-major so that each (block, plane) reduction reads
+// one contiguous run.
+template <int RPW, int PMAX>
+__device__ __forceinline__ void importance_partials(const float (&wraw)[RPW][PMAX], int P, int w,
+                                                    float *__restrict__ imp_part) {
+  __syncthreads();
+  if ((int)threadIdx.x < P) {
+    float s = 0.f;
+#pragma unroll 4
+    for (int j = 0; j < RPW; ++j) s += wraw[j][threadIdx.x];
+    imp_part[(int64_t)threadIdx.x * gridDim.x + w] = s;
+  }
+}
+
+// One thread per 8 consecutive d of a row-head.  IMP: per-block placement and importance
+// partials.  lse_rowmajor: the merged lse goes out as [B, S_q, H] (a cache plane) instead of
+// [B, H, S_q].
+template <int D, int PMAX, bool IMP>
 __global__ __launch_bounds__(256) void state_merge_kernel(
     const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, u16 *__restrict__ out,
     float *__restrict__ lse_out, const int S_q, const int H, const int P, const int64_t total_rh,
-    const int64_t plane_o, const int64_t plane_lse, const int chunk) {
+    const int64_t plane_o, const int64_t plane_lse, const int chunk, const int lse_rowmajor, const MergeGrid g,
+    float *__restrict__ imp_part) {
   constexpr int TPR = D / 8;
   constexpr int RPW = 256 / TPR;
-  const int64_t rh = (int64_t)lse_chunked_item(chunk) * RPW + threadIdx.x / TPR;
-  if (rh >= total_rh) return;
+  const int w = lse_chunked_item(chunk);
+  int64_t rh0, rh_end;
+  merge_rows<RPW>(g, w, S_q, H, total_rh, rh0, rh_end);
+  const int64_t rh = rh0 + threadIdx.x / TPR;
+  const bool valid = rh < rh_end;
+  if (!IMP && !valid) return;
   const int c = threadIdx.x % TPR;
-  const int64_t br = rh / H;  // b * S_q + r
-  const int h = (int)(rh - br * H);
-  const int64_t b = br / S_q;
-  const int64_t r = br - b * S_q;
-  const int64_t li = (b * H + h) * S_q + r;
 
   __shared__ float wts_all[RPW][PMAX];
   float *wts = wts_all[threadIdx.x / TPR];
-  const float L = group_merge_weights<TPR, PMAX, false>(cache_lse, nullptr, li, plane_lse, P, c, wts);
+  const float L = group_merge_weights<TPR, PMAX, false>(cache_lse, nullptr, rh, plane_lse, P, c, valid, wts, nullptr);
 
-  float acc[8];
+  if (valid) {
+    float acc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  const u16 *src = cache_o + rh * D + 8 * c;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const u16 *src = cache_o + rh * D + 8 * c;
 #pragma unroll
-  for (int p = 0; p < PMAX; ++p) {
-    if (p < P) {
-      const float w = wts[p];
-      const u32x4 u = __builtin_nontemporal_load((const u32x4 *)(src + p * plane_o));
-      const uint32_t x[4] = {u[0], u[1], u[2], u[3]};
+    for (int p = 0; p < PMAX; ++p) {
+      if (p < P) {
+        const float wp = wts[p];
+        const u32x4 u = __builtin_nontemporal_load((const u32x4 *)(src + p * plane_o));
+        const uint32_t x[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        acc[2 * t] += w * bf16_bits_to_f32(x[t] & 0xffffu);
-        acc[2 * t + 1] += w * bf16_bits_to_f32(x[t] >> 16);
+        for (int t = 0; t < 4; ++t) {
+          acc[2 * t] += wp * bf16_bits_to_f32(x[t] & 0xffffu);
+          acc[2 * t + 1] += wp * bf16_bits_to_f32(x[t] >> 16);
+        }
       }
     }
+    uint4 res;
+    res.x = pack_bf16x2(acc[0], acc[1]);
+    res.y = pack_bf16x2(acc[2], acc[3]);
+    res.z = pack_bf16x2(acc[4], acc[5]);
+    res.w = pack_bf16x2(acc[6], acc[7]);
+    __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
+    if (c == 0) {
+      const int64_t br = rh / H;
+      const int h = (int)(rh - br * H);
+      const int64_t b = br / S_q;
+      const int64_t r = br - b * S_q;
+      lse_out[lse_rowmajor ? rh : (b * H + h) * S_q + r] = L;
+    }
   }
-  uint4 res;
-  res.x = pack_bf16x2(acc[0], acc[1]);
-  res.y = pack_bf16x2(acc[2], acc[3]);
-  res.z = pack_bf16x2(acc[4], acc[5]);
-  res.w = pack_bf16x2(acc[6], acc[7]);
-  __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
-  if (c == 0) lse_out[li] = L;
+  if constexpr (IMP) importance_partials<RPW, PMAX>(wts_all, P, w, imp_part);
 }
 
 // State merge over the compressed cache: per row-head, plane p holds e4m3 codes and a scale
 // s_p; the scale folds into the merge weight, w_p = s_p e^{lse_p - lse}.  One thread per
 // kFp8Dpt consecutive d (kFp8Dpt-byte code loads, non-temporal; bf16 output stores).
 constexpr int kFp8Dpt = DIT_MERGE_FP8_DPT;
-template <int D, int PMAX>
+template <int D, int PMAX, bool IMP>
 __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
     const uint8_t *__restrict__ cache_q8, const float *__restrict__ cache_scale,
     const float *__restrict__ cache_lse, u16 *__restrict__ out, float *__restrict__ lse_out,
     const int S_q, const int H, const int P, const int64_t total_rh, const int64_t plane_o,
-    const int64_t plane_lse, const int chunk) {
+    const int64_t plane_lse, const int chunk, const MergeGrid g, float *__restrict__ imp_part) {
   constexpr int TPR = D / kFp8Dpt;
   constexpr int RPW = 256 / TPR;
   constexpr int NW = kFp8Dpt / 4;  // 32-bit code words per thread and plane
-  const int64_t rh = (int64_t)lse_chunked_item(chunk) * RPW + threadIdx.x / TPR;
-  if (rh >= total_rh) return;
+  const int w = lse_chunked_item(chunk);
+  int64_t rh0, rh_end;
+  merge_rows<RPW>(g, w, S_q, H, total_rh, rh0, rh_end);
+  const int64_t rh = rh0 + threadIdx.x / TPR;
+  const bool valid = rh < rh_end;
+  if (!IMP && !valid) return;
   const int c = threadIdx.x % TPR;
-  const int64_t br = rh / H;
-  const int h = (int)(rh - br * H);
-  const int64_t b = br / S_q;
-  const int64_t r = br - b * S_q;
-  const int64_t li = (b * H + h) * S_q + r;
 
   __shared__ float wts_all[RPW][PMAX];
+  __shared__ float wraw_all[IMP ? RPW : 1][IMP ? PMAX : 1];
   float *wts = wts_all[threadIdx.x / TPR];
-  const float L = group_merge_weights<TPR, PMAX, true>(cache_lse, cache_scale, li, plane_lse, P, c, wts);
+  const float L = group_merge_weights<TPR, PMAX, true>(cache_lse, cache_scale, rh, plane_lse, P, c, valid, wts,
+                                                       IMP ? &wraw_all[threadIdx.x / TPR][0] : nullptr);
 
-  float acc[kFp8Dpt];
+  if (valid) {
+    float acc[kFp8Dpt];
 #pragma unroll
-  for (int e = 0; e < kFp8Dpt; ++e) acc[e] = 0.f;
-  const uint8_t *src = cache_q8 + rh * D + kFp8Dpt * c;
+    for (int e = 0; e < kFp8Dpt; ++e) acc[e] = 0.f;
+    const uint8_t *src = cache_q8 + rh * D + kFp8Dpt * c;
 #pragma unroll
-  for (int p = 0; p < PMAX; ++p) {
-    if (p < P) {
-      const float w = wts[p];
-      uint32_t u[NW];
-      if constexpr (NW >= 4) {
+    for (int p = 0; p < PMAX; ++p) {
+      if (p < P) {
+        const float wp = wts[p];
+        uint32_t u[NW];
+        if constexpr (NW >= 4) {
 #pragma unroll
-        for (int q = 0; q < NW / 4; ++q) {
-          const u32x4 v4 = __builtin_nontemporal_load((const u32x4 *)(src + p * plane_o) + q);
-          u[4 * q + 0] = v4[0];
-          u[4 * q + 1] = v4[1];
-          u[4 * q + 2] = v4[2];
-          u[4 * q + 3] = v4[3];
+          for (int q = 0; q < NW / 4; ++q) {
+            const u32x4 v4 = __builtin_nontemporal_load((const u32x4 *)(src + p * plane_o) + q);
+            u[4 * q + 0] = v4[0];
+            u[4 * q + 1] = v4[1];
+            u[4 * q + 2] = v4[2];
+            u[4 * q + 3] = v4[3];
+          }
+        } else {
+          const u32x2 v2 = __builtin_nontemporal_load((const u32x2 *)(src + p * plane_o));
+          u[0] = v2[0];
+          u[1] = v2[1];
         }
-      } else {
-        const u32x2 v2 = __builtin_nontemporal_load((const u32x2 *)(src + p * plane_o));
-        u[0] = v2[0];
-        u[1] = v2[1];
-      }
 #pragma unroll
-      for (int t = 0; t < NW; ++t) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], true);
-        acc[4 * t + 0] += w * lo[0];
-        acc[4 * t + 1] += w * lo[1];
-        acc[4 * t + 2] += w * hi[0];
-        acc[4 * t + 3] += w * hi[1];
+        for (int t = 0; t < NW; ++t) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], true);
+          acc[4 * t + 0] += wp * lo[0];
+          acc[4 * t + 1] += wp * lo[1];
+          acc[4 * t + 2] += wp * hi[0];
+          acc[4 * t + 3] += wp * hi[1];
+        }
       }
     }
-  }
 #pragma unroll
-  for (int q = 0; q < kFp8Dpt / 8; ++q)
-    __builtin_nontemporal_store(u32x4{pack_bf16x2(acc[8 * q + 0], acc[8 * q + 1]), pack_bf16x2(acc[8 * q + 2], acc[8 * q + 3]),
-                                      pack_bf16x2(acc[8 * q + 4], acc[8 * q + 5]), pack_bf16x2(acc[8 * q + 6], acc[8 * q + 7])},
-                                (u32x4 *)(out + rh * D + kFp8Dpt * c + 8 * q));
-  if (c == 0) lse_out[li] = L;
-}
-
-template <int D>
-hipError_t merge_fp8_dispatch(int P, const void *cache_q8, const float *cache_scale, const float *cache_lse,
-                              void *out, float *lse, int B, int S_q, int H, hipStream_t stream) {
-  const int64_t total_rh = (int64_t)B * S_q * H;
-  if (total_rh == 0) return hipSuccess;
-  constexpr int RPW = 256 / (D / kFp8Dpt);
-  const int64_t nwg = (total_rh + RPW - 1) / RPW;
-  const int64_t plane_o = total_rh * D;
-  const int64_t plane_lse = total_rh;
-  const int chunk = merge_chunk(RPW, H);
-  dim3 grid((unsigned)nwg), block(256);
-  const uint8_t *cq = (const uint8_t *)cache_q8;
-  u16 *oo = (u16 *)out;
-  if (P <= 8)
-    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 8>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
-  else if (P <= 16)
-    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 16>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
-  else if (P <= 32)
-    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 32>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
-  else
-    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 64>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
-  return hipGetLastError();
+    for (int q = 0; q < kFp8Dpt / 8; ++q)
+      __builtin_nontemporal_store(u32x4{pack_bf16x2(acc[8 * q + 0], acc[8 * q + 1]), pack_bf16x2(acc[8 * q + 2], acc[8 * q + 3]),
+                                        pack_bf16x2(acc[8 * q + 4], acc[8 * q + 5]), pack_bf16x2(acc[8 * q + 6], acc[8 * q + 7])},
+                                  (u32x4 *)(out + rh * D + kFp8Dpt * c + 8 * q));
+    if (c == 0) {
+      const int64_t br = rh / H;
+      const int h = (int)(rh - br * H);
+      const int64_t b = br / S_q;
+      const int64_t r = br - b * S_q;
+      lse_out[(b * H + h) * S_q + r] = L;
+    }
+  }
+  if constexpr (IMP) importance_partials<RPW, PMAX>(wraw_all, P, w, imp_part);
 }
 
 // Masked merge: as state_merge_kernel, but row r of query block i combines only the planes
-// selected for block i, plus an optional extra state (a partial composition made earlier).
+// selected for block i, plus an optional extra state (a partial composition made earlier,
+// its lse in the [B, H, S_q] layout of a merged output).
 // Used to pre-merge the reused states on a second stream while the attention kernel
 // recomputes the others, and to finish with the fresh states and that partial.
 template <int D, int PMAX>
@@ -854,7 +956,7 @@ __global__ __launch_bounds__(256) void state_merge_masked_kernel(
   const int h = (int)(rh - br * H);
   const int64_t b = br / S_q;
   const int r = (int)(br - b * S_q);
-  const int64_t li = (b * H + h) * S_q + r;
+  const int64_t lo_idx = (b * H + h) * S_q + r;
   // block of row r: last i with q_off[i] <= r
   int lo = 0, hi = sel.n_qb - 1;
   while (lo < hi) {
@@ -865,8 +967,8 @@ __global__ __launch_bounds__(256) void state_merge_masked_kernel(
 
   __shared__ float wts_all[RPW][PMAX + 1];
   float *wts = wts_all[threadIdx.x / TPR];
-  const float L = group_merge_weights<TPR, PMAX, false>(cache_lse, nullptr, li, plane_lse, P, c, wts, pm,
-                                                        sel.has_extra ? extra_lse : nullptr);
+  const float L = group_merge_weights<TPR, PMAX, false>(cache_lse, nullptr, rh, plane_lse, P, c, true, wts, nullptr,
+                                                        pm, sel.has_extra ? extra_lse : nullptr, lo_idx);
 
   float acc[8];
 #pragma unroll
@@ -920,7 +1022,7 @@ __global__ __launch_bounds__(256) void state_merge_masked_kernel(
   res.z = pack_bf16x2(acc[4], acc[5]);
   res.w = pack_bf16x2(acc[6], acc[7]);
   __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
-  if (c == 0) lse_out[li] = L;
+  if (c == 0) lse_out[lo_idx] = L;
 }
 
 template <int D>
@@ -961,9 +1063,11 @@ __device__ __forceinline__ float block_sum_256(float x, float *sh) {
   return sh[0];
 }
 
-// Importance: one workgroup of 1024 threads per (batch, block i, partition p).  Each thread
-// walks the block's rows of every head with four independent loads in flight (rows r,
-// r + 1024, r + 2048, r + 3072), then a fixed-order tree sums the threads.
+// Importance from the stored lse planes (a second pass, for callers without a workspace):
+// one workgroup of 1024 threads per (batch, block i, partition p).  Each thread walks the
+// block's row-heads e = (r - q_off[i]) H + h with four independent loads in flight (e,
+// e + 1024, e + 2048, e + 3072): cache_lse of the plane is contiguous over e, the merged lse
+// [B, H, S_q] is gathered.  A fixed-order tree sums the threads.
 constexpr int kImpThreads = 1024;
 __device__ __forceinline__ float block_sum_1024(float x, float *sh) {
   sh[threadIdx.x] = x;
@@ -985,27 +1089,44 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(
   const int b = blockIdx.y;
   const int r0 = blocks.q_off[i];
   const int nr = blocks.q_off[i + 1] - r0;
-  const float *cl = cache_lse + ((int64_t)p * B + b) * H * S_q + r0;
+  const int64_t n = (int64_t)nr * H;
+  const float *cl = cache_lse + (((int64_t)p * B + b) * S_q + r0) * H;
   const float *ml = lse + (int64_t)b * H * S_q + r0;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int h = 0; h < H; ++h) {
-    const float *clh = cl + (int64_t)h * S_q;
-    const float *mlh = ml + (int64_t)h * S_q;
-    for (int r = threadIdx.x; r < nr; r += 4 * kImpThreads) {
+  for (int64_t e = threadIdx.x; e < n; e += 4 * kImpThreads) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int rr = r + u * kImpThreads;
-        if (rr < nr) {
-          const float a = clh[rr];
-          const float t = mlh[rr];
-          acc[u] += (a > -INFINITY && t > -INFINITY) ? __expf(a - t) : 0.f;
-        }
+    for (int u = 0; u < 4; ++u) {
+      const int64_t ee = e + u * kImpThreads;
+      if (ee < n) {
+        const int r = (int)(ee / H);
+        const int h = (int)(ee - (int64_t)r * H);
+        const float a = cl[ee];
+        const float t = ml[(int64_t)h * S_q + r];
+        acc[u] += (a > -INFINITY && t > -INFINITY) ? __expf(a - t) : 0.f;
       }
     }
   }
   const float tot = block_sum_1024((acc[0] + acc[1]) + (acc[2] + acc[3]), sh);
-  const int64_t n = (int64_t)nr * H;
   if (threadIdx.x == 0) out[((int64_t)b * blocks.n_qb + i) * P + p] = n > 0 ? tot / (float)n : 0.f;
+}
+
+// Importance from the merge's partials: one workgroup per (batch, block i, partition p) sums
+// plane p's partials of block i's merge workgroups (a contiguous run) in a fixed order.
+__global__ __launch_bounds__(256) void importance_finalize_kernel(const float *__restrict__ part, const int P,
+                                                                  const int H, const int nwg, const MergeGrid g,
+                                                                  float *__restrict__ out) {
+  __shared__ float sh[256];
+  const int p = blockIdx.x % P;
+  const int i = blockIdx.x / P;
+  const int b = blockIdx.y;
+  const int w0 = b * g.wg_per_batch + g.wg_prefix[i];
+  const int w1 = b * g.wg_per_batch + g.wg_prefix[i + 1];
+  const float *src = part + (int64_t)p * nwg;
+  float acc = 0.f;
+  for (int w = w0 + (int)threadIdx.x; w < w1; w += 256) acc += src[w];
+  const float tot = block_sum_256(acc, sh);
+  const int64_t n = (int64_t)(g.q_off[i + 1] - g.q_off[i]) * H;
+  if (threadIdx.x == 0) out[((int64_t)b * g.n_qb + i) * P + p] = tot / (float)n;
 }
 
 // Local change: one workgroup per (batch, block i) sums the (tile, head) partials.
@@ -1029,68 +1150,178 @@ __global__ __launch_bounds__(256) void delta_finalize_kernel(const float *__rest
   if (threadIdx.x == 0) out[(int64_t)b * blocks.n_qb + i] = sqrtf(tn) / sqrtf(td);
 }
 
-template <int D>
-hipError_t merge_dispatch(int P, const void *cache_o, const float *cache_lse, void *out, float *lse,
-                          int B, int S_q, int H, hipStream_t stream) {
+// Placement of a merge launch: plain over all row-heads, or per block when importance
+// partials are wanted (imp_blocks non-null).
+MergeGrid make_merge_grid(int RPW, const BlockDesc *imp_blocks, int B, int S_q, int H, int64_t &nwg) {
+  MergeGrid g;
+  memset(&g, 0, sizeof(g));
+  const int64_t total_rh = (int64_t)B * S_q * H;
+  if (imp_blocks == nullptr) {
+    nwg = (total_rh + RPW - 1) / RPW;
+    return g;
+  }
+  g.n_qb = imp_blocks->n_qb;
+  for (int i = 0; i <= g.n_qb; ++i) g.q_off[i] = imp_blocks->q_off[i];
+  for (int i = 0; i < g.n_qb; ++i) {
+    const int64_t n = (int64_t)(g.q_off[i + 1] - g.q_off[i]) * H;
+    g.wg_prefix[i + 1] = g.wg_prefix[i] + (int32_t)((n + RPW - 1) / RPW);
+  }
+  g.wg_per_batch = g.wg_prefix[g.n_qb];
+  nwg = (int64_t)B * g.wg_per_batch;
+  return g;
+}
+
+hipError_t launch_importance_finalize(const float *imp_part, int P, int H, int B, int64_t nwg, const MergeGrid &g,
+                                      float *importance_out, hipStream_t stream) {
+  dim3 grid((unsigned)(g.n_qb * P), (unsigned)B), block(256);
+  hipLaunchKernelGGL(importance_finalize_kernel, grid, block, 0, stream, imp_part, P, H, (int)nwg, g,
+                     importance_out);
+  return hipGetLastError();
+}
+
+template <int D, bool IMP>
+hipError_t merge_dispatch(int P, const void *cache_o, const float *cache_lse, void *out, float *lse, int B,
+                          int S_q, int H, bool lse_rowmajor, const BlockDesc *imp_blocks, float *imp_part,
+                          float *importance_out, hipStream_t stream) {
   const int64_t total_rh = (int64_t)B * S_q * H;
   if (total_rh == 0) return hipSuccess;
   constexpr int RPW = 256 / (D / 8);
-  const int64_t nwg = (total_rh + RPW - 1) / RPW;
+  int64_t nwg = 0;
+  const MergeGrid g = make_merge_grid(RPW, IMP ? imp_blocks : nullptr, B, S_q, H, nwg);
   const int64_t plane_o = total_rh * D;
   const int64_t plane_lse = total_rh;
   const int chunk = merge_chunk(RPW, H);
   dim3 grid((unsigned)nwg), block(256);
   const u16 *co = (const u16 *)cache_o;
   u16 *oo = (u16 *)out;
+  const int rm = lse_rowmajor ? 1 : 0;
   if (P <= 8)
-    hipLaunchKernelGGL((state_merge_kernel<D, 8>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
+    hipLaunchKernelGGL((state_merge_kernel<D, 8, IMP>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk, rm, g, imp_part);
   else if (P <= 16)
-    hipLaunchKernelGGL((state_merge_kernel<D, 16>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
+    hipLaunchKernelGGL((state_merge_kernel<D, 16, IMP>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk, rm, g, imp_part);
   else if (P <= 32)
-    hipLaunchKernelGGL((state_merge_kernel<D, 32>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
+    hipLaunchKernelGGL((state_merge_kernel<D, 32, IMP>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk, rm, g, imp_part);
   else
-    hipLaunchKernelGGL((state_merge_kernel<D, 64>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk);
-  return hipGetLastError();
+    hipLaunchKernelGGL((state_merge_kernel<D, 64, IMP>), grid, block, 0, stream, co, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk, rm, g, imp_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !IMP) return e;
+  return launch_importance_finalize(imp_part, P, H, B, nwg, g, importance_out, stream);
+}
+
+template <int D, bool IMP>
+hipError_t merge_fp8_dispatch(int P, const void *cache_q8, const float *cache_scale, const float *cache_lse,
+                              void *out, float *lse, int B, int S_q, int H, const BlockDesc *imp_blocks,
+                              float *imp_part, float *importance_out, hipStream_t stream) {
+  const int64_t total_rh = (int64_t)B * S_q * H;
+  if (total_rh == 0) return hipSuccess;
+  constexpr int RPW = 256 / (D / kFp8Dpt);
+  int64_t nwg = 0;
+  const MergeGrid g = make_merge_grid(RPW, IMP ? imp_blocks : nullptr, B, S_q, H, nwg);
+  const int64_t plane_o = total_rh * D;
+  const int64_t plane_lse = total_rh;
+  const int chunk = merge_chunk(RPW, H);
+  dim3 grid((unsigned)nwg), block(256);
+  const uint8_t *cq = (const uint8_t *)cache_q8;
+  u16 *oo = (u16 *)out;
+  if (P <= 8)
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 8, IMP>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk, g, imp_part);
+  else if (P <= 16)
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 16, IMP>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk, g, imp_part);
+  else if (P <= 32)
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 32, IMP>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk, g, imp_part);
+  else
+    hipLaunchKernelGGL((state_merge_fp8_kernel<D, 64, IMP>), grid, block, 0, stream, cq, cache_scale, cache_lse, oo, lse, S_q, H, P, total_rh, plane_o, plane_lse, chunk, g, imp_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !IMP) return e;
+  return launch_importance_finalize(imp_part, P, H, B, nwg, g, importance_out, stream);
 }
 
 }  // namespace
 
+int64_t merge_workgroups(int D, bool fp8_cache, const BlockDesc *imp_blocks, int B, int S_q, int H) {
+  const int rpw = fp8_cache ? 256 / (D / kFp8Dpt) : 256 / (D / 8);
+  int64_t nwg = 0;
+  make_merge_grid(rpw, imp_blocks, B, S_q, H, nwg);
+  return nwg;
+}
+
+namespace {
+// Zero `n` ints (the schedule counters of an attention launch; a kernel rather than a memset
+// so that the sequence can be captured in a graph).
+__global__ __launch_bounds__(64) void clear_ints_kernel(int *__restrict__ p, int n) {
+  // agent-scope stores: the counters are then read and updated by every XCD
+  if ((int)threadIdx.x < n) __hip_atomic_store(&p[threadIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+}  // namespace
+
+AttnLaunch attention_launch_shape(const AttnDesc &desc, bool balanced) {
+  AttnLaunch L;
+  L.n_items = (int64_t)desc.B * desc.H * desc.items_per_head;
+  L.balanced = balanced && L.n_items >= kBalanceMinItems;
+  if (!L.balanced) {
+    L.static_per = 0;
+    L.workgroups = L.n_items;
+    return L;
+  }
+  const int64_t per_max = (L.n_items + 7) / 8;
+  L.static_per = (int32_t)(per_max * kBalanceStaticPercent / 100);
+  L.workgroups = 8 * (per_max + (per_max * kBalanceSparePercent + 99) / 100 + 1);
+  return L;
+}
+
 hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, const void *k, const void *v,
                                       void *cache_o, float *cache_scale, float *cache_lse, float *delta_partials,
-                                      const AttnDesc &desc, float scale_log2, hipStream_t stream) {
-  const int64_t nwg = (int64_t)desc.B * desc.H * desc.items_per_head;
-  if (nwg == 0) return hipSuccess;
+                                      int *sched, const AttnDesc &desc, float scale_log2, hipStream_t stream) {
+  const AttnLaunch L = attention_launch_shape(desc, sched != nullptr);
+  if (L.n_items == 0) return hipSuccess;
   (void)hipGetLastError();
-  dim3 grid((unsigned)nwg), block(kWaves * 64);
+  int *sc = L.balanced ? sched : nullptr;
+  if (sc != nullptr) {
+    hipLaunchKernelGGL(clear_ints_kernel, dim3(1), dim3(64), 0, stream, sc, kSchedInts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((unsigned)L.workgroups), block(kWaves * 64);
   const u16 *qq = (const u16 *)q, *kk = (const u16 *)k, *vv = (const u16 *)v;
+  const int sp = L.static_per;
   if (D == 128 && !fp8_cache)
     hipLaunchKernelGGL((partition_attention_kernel<128, false>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
-                       cache_lse, delta_partials, desc, scale_log2);
+                       cache_lse, delta_partials, desc, scale_log2, sc, sp);
   else if (D == 128)
     hipLaunchKernelGGL((partition_attention_kernel<128, true>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
-                       cache_lse, delta_partials, desc, scale_log2);
+                       cache_lse, delta_partials, desc, scale_log2, sc, sp);
   else if (!fp8_cache)
     hipLaunchKernelGGL((partition_attention_kernel<64, false>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
-                       cache_lse, delta_partials, desc, scale_log2);
+                       cache_lse, delta_partials, desc, scale_log2, sc, sp);
   else
     hipLaunchKernelGGL((partition_attention_kernel<64, true>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
-                       cache_lse, delta_partials, desc, scale_log2);
+                       cache_lse, delta_partials, desc, scale_log2, sc, sp);
   return hipGetLastError();
 }
 
 hipError_t launch_state_merge_fp8(int D, int P, const void *cache_q8, const float *cache_scale,
                                   const float *cache_lse, void *out, float *lse, int B, int S_q, int H,
+                                  const BlockDesc *imp_blocks, float *imp_part, float *importance_out,
                                   hipStream_t stream) {
   (void)hipGetLastError();
-  if (D == 128) return merge_fp8_dispatch<128>(P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, stream);
-  return merge_fp8_dispatch<64>(P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, stream);
+  const bool imp = imp_blocks != nullptr;
+  if (D == 128)
+    return imp ? merge_fp8_dispatch<128, true>(P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, imp_blocks, imp_part, importance_out, stream)
+               : merge_fp8_dispatch<128, false>(P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, nullptr, nullptr, nullptr, stream);
+  return imp ? merge_fp8_dispatch<64, true>(P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, imp_blocks, imp_part, importance_out, stream)
+             : merge_fp8_dispatch<64, false>(P, cache_q8, cache_scale, cache_lse, out, lse, B, S_q, H, nullptr, nullptr, nullptr, stream);
 }
 
 hipError_t launch_state_merge(int D, int P, const void *cache_o, const float *cache_lse, void *out,
-                              float *lse, int B, int S_q, int H, hipStream_t stream) {
+                              float *lse, int B, int S_q, int H, bool lse_rowmajor, const BlockDesc *imp_blocks,
+                              float *imp_part, float *importance_out, hipStream_t stream) {
   (void)hipGetLastError();
-  if (D == 128) return merge_dispatch<128>(P, cache_o, cache_lse, out, lse, B, S_q, H, stream);
-  return merge_dispatch<64>(P, cache_o, cache_lse, out, lse, B, S_q, H, stream);
+  const bool imp = imp_blocks != nullptr;
+  if (D == 128)
+    return imp ? merge_dispatch<128, true>(P, cache_o, cache_lse, out, lse, B, S_q, H, lse_rowmajor, imp_blocks, imp_part, importance_out, stream)
+               : merge_dispatch<128, false>(P, cache_o, cache_lse, out, lse, B, S_q, H, lse_rowmajor, nullptr, nullptr, nullptr, stream);
+  return imp ? merge_dispatch<64, true>(P, cache_o, cache_lse, out, lse, B, S_q, H, lse_rowmajor, imp_blocks, imp_part, importance_out, stream)
+             : merge_dispatch<64, false>(P, cache_o, cache_lse, out, lse, B, S_q, H, lse_rowmajor, nullptr, nullptr, nullptr, stream);
 }
 
 hipError_t launch_state_merge_masked(int D, int P, const void *cache_o, const float *cache_lse,

@@ -75,14 +75,46 @@ struct BlockDesc {
   int32_t tile_prefix[DIT_MAX_BLOCKS + 1];
 };
 
+// Work balancing of the attention launch across the 8 XCDs (which run at different clocks):
+// the first kBalanceStaticPercent % of each XCD's items are placed statically, the rest are
+// claimed at run time through kSchedInts counters in the workspace; the grid holds
+// kBalanceSparePercent % spare workgroups per XCD for the claims.  Launches of fewer than
+// kBalanceMinItems items (about two rounds of the chip) stay static.
+#ifndef DIT_BALANCE_STATIC_PERCENT
+#define DIT_BALANCE_STATIC_PERCENT 80
+#endif
+#ifndef DIT_BALANCE_SPARE_PERCENT
+#define DIT_BALANCE_SPARE_PERCENT 12
+#endif
+constexpr int kBalanceStaticPercent = DIT_BALANCE_STATIC_PERCENT;
+constexpr int kBalanceSparePercent = DIT_BALANCE_SPARE_PERCENT;
+constexpr int64_t kBalanceMinItems = 1536;
+constexpr int kSchedInts = 8;
+constexpr size_t kSchedBytes = 256;  // workspace bytes reserved for the counters
+
+struct AttnLaunch {
+  int64_t n_items;      // (batch, head, partition, block, tile) items
+  int64_t workgroups;   // grid size
+  int32_t static_per;   // statically placed items per XCD
+  bool balanced;
+};
+AttnLaunch attention_launch_shape(const AttnDesc &desc, bool balanced);
+
 // fp8_cache: cache_o holds e4m3 codes (1 byte per element) and cache_scale one scale per
 // (partition, batch, head, row); otherwise cache_o is bf16 and cache_scale is unused.
+// sched: kSchedInts ints of device memory for the balanced schedule, or NULL (static).
 hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, const void *k, const void *v,
                                       void *cache_o, float *cache_scale, float *cache_lse, float *delta_partials,
-                                      const AttnDesc &desc, float scale_log2, hipStream_t stream);
+                                      int *sched, const AttnDesc &desc, float scale_log2, hipStream_t stream);
 
+// Merges.  The cache's lse (and scale) planes are [P, B, S_q, H]; the merged lse goes out as
+// [B, H, S_q], or, with lse_rowmajor, as [B, S_q, H] (a cache plane: compose).  With
+// imp_blocks non-null the merge also writes importance partials (imp_part: P floats per
+// merge workgroup, merge_workgroups(...) of them) and finishes the importance into
+// importance_out [B, n_qb, P].
 hipError_t launch_state_merge_fp8(int D, int P, const void *cache_q8, const float *cache_scale,
                                   const float *cache_lse, void *out, float *lse, int B, int S_q, int H,
+                                  const BlockDesc *imp_blocks, float *imp_part, float *importance_out,
                                   hipStream_t stream);
 
 // Plane selection of a masked merge: row r of block i merges plane p when bit p of
@@ -99,7 +131,13 @@ hipError_t launch_state_merge_masked(int D, int P, const void *cache_o, const fl
                                      void *out, float *lse, int B, int S_q, int H, hipStream_t stream);
 
 hipError_t launch_state_merge(int D, int P, const void *cache_o, const float *cache_lse,
-                              void *out, float *lse, int B, int S_q, int H, hipStream_t stream);
+                              void *out, float *lse, int B, int S_q, int H, bool lse_rowmajor,
+                              const BlockDesc *imp_blocks, float *imp_part, float *importance_out,
+                              hipStream_t stream);
+
+// Workgroups of a merge launch (with imp_blocks: the per-block placement of the importance
+// partials).
+int64_t merge_workgroups(int D, bool fp8_cache, const BlockDesc *imp_blocks, int B, int S_q, int H);
 
 hipError_t launch_importance(const float *cache_lse, const float *lse, int B, int S_q, int H,
                              int P, const BlockDesc &blocks, float *importance_out,

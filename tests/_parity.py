@@ -123,7 +123,9 @@ class GpuRun:
         return self.sa.lse[0][:, torch.as_tensor(rows, device="cuda")].double().cpu().numpy()
 
     def cache_lse_rows(self, rows) -> np.ndarray:
-        return self.sa.cache_lse[:, 0][:, :, torch.as_tensor(rows, device="cuda")].double().cpu().numpy()
+        """Cached lse of the rows as [P, H, n] (the oracle's layout; the device keeps [P, B, S_q, H])."""
+        a = self.sa.cache_lse[:, 0][:, torch.as_tensor(rows, device="cuda"), :].double().cpu().numpy()
+        return np.ascontiguousarray(np.transpose(a, (0, 2, 1)))
 
     def cache_o_rows(self, rows) -> np.ndarray:
         return bf16_to_f64(self.sa.cache_o[:, 0][:, torch.as_tensor(rows, device="cuda")])

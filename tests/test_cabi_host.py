@@ -45,7 +45,11 @@ def test_status_strings(L):
 
 
 def test_workspace_bytes(L):
-    assert L.dit_attn_workspace_bytes(1, 75600, 40, 128, 16, 16) == (591 + 16) * 40 * 8  # 128-row query tiles
+    # 256 bytes of schedule counters, the local-change partials: (591 + 16) 128-row query
+    # tiles x 40 heads x 2 floats, then from the next 256-byte boundary the merge's importance
+    # partials: (75,600 x 40 / 16 + 16) merge workgroups x 16 planes x 4 bytes
+    delta = (591 + 16) * 40 * 8
+    assert L.dit_attn_workspace_bytes(1, 75600, 40, 128, 16, 16) == (256 + delta + 255) // 256 * 256 + (189000 + 16) * 16 * 4
     assert L.dit_attn_workspace_bytes(1, 100, 4, 96, 1, 1) == 0      # unsupported D
     assert L.dit_attn_workspace_bytes(1, 100, 4, 64, 0, 1) == 0      # no blocks
     assert L.dit_attn_workspace_bytes(1, 100, 4, 64, 1, 65) == 0     # too many partitions
@@ -103,6 +107,17 @@ def test_attention_grid_beyond_32_bit_work_items(L):
     assert _call(L, S_q=S_q, S_kv=64, H=40, D=128, qo=(0, S_q), ko=tuple(range(65)), rec=(1,) * 64) == -2
 
 
+def test_importance_needs_the_workspace(L):
+    """The one-call step computes the importance inside the merge: importance_out without a
+    workspace large enough for the partials is DIT_ERR_WORKSPACE."""
+    i32 = lambda s: (ctypes.c_int32 * len(s))(*s)
+    u8 = lambda s: (ctypes.c_uint8 * len(s))(*s)
+    args = lambda ws, wsb: (1, 1, 1, 1, 8, 8, 1, 64, i32([0, 8]), 1, i32([0, 4, 8]), 2, i32([0]), u8([1, 0]), None,
+                           1, 1, 1, 1, 0.0, 1, None, ws, wsb, None)
+    assert L.dit_attn_partitioned(*args(None, 0)) == -6
+    assert L.dit_attn_partitioned(*args(1, 256)) == -6
+
+
 def _tile_span_limit(D):
     """Largest H*D whose 32-key tile rows (31 row strides of H*D bf16 plus one row of D)
     fit a 31-bit buffer range, and H*D must be a multiple of D."""
@@ -127,7 +142,7 @@ def test_merge_does_not_apply_the_tile_range_limit(L):
     """Only the attention calls copy K/V tiles: a merge with H*D above the tile limit passes
     the shape check (it fails later, on a NULL output pointer)."""
     H = _tile_span_limit(128) // 128 + 1
-    assert L.dit_state_merge(1, 1, 1, 8, H, 128, 2, None, 1, None) == -1
+    assert L.dit_state_merge(1, 1, 1, 8, H, 128, 2, None, 1, None, 0, None, None, 0, None) == -1
 
 
 def test_too_many_blocks_or_partitions(L):
@@ -165,15 +180,24 @@ def _u8(s):
     # dit_partition_attention(q, k, v, B, S_q, S_kv, H, D, qo, n_qb, ko, P, local, rec, valid, o, lse, sm, ws, wsb, st)
     (lambda L: L.dit_partition_attention(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
                                          _u8([1, 0]), _u8([1, 0]), 1, 1, 0.0, None, 0, None), -5),
-    # dit_state_merge_fp8(q8, scale, lse, B, S_q, H, D, P, out, lse_out, st)
-    (lambda L: L.dit_state_merge_fp8(1, None, 1, 1, 8, 1, 64, 2, 1, 1, None), -1),
-    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 64, 65, 1, 1, None), -2),
-    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 48, 2, 1, 1, None), -7),
-    # dit_state_merge(o, lse, B, S_q, H, D, P, out, lse_out, st)
-    (lambda L: L.dit_state_merge(1, 1, 1, 8, 1, 64, 0, 1, 1, None), -2),
-    (lambda L: L.dit_state_merge(1, None, 1, 8, 1, 64, 2, 1, 1, None), -1),
+    # dit_state_merge_fp8(q8, scale, lse, B, S_q, H, D, P, out, lse_out, qo, n_qb, imp, ws, wsb, st)
+    (lambda L: L.dit_state_merge_fp8(1, None, 1, 1, 8, 1, 64, 2, 1, 1, None, 0, None, None, 0, None), -1),
+    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 64, 65, 1, 1, None, 0, None, None, 0, None), -2),
+    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 48, 2, 1, 1, None, 0, None, None, 0, None), -7),
+    # importance in the fp8 merge: offsets, then the workspace
+    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 64, 2, 1, 1, _i32([0, 9]), 1, 1, 1, 1 << 20, None), -3),
+    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 64, 2, 1, 1, _i32([0, 8]), 1, 1, None, 0, None), -6),
+    (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 64, 2, 1, 1, _i32([0, 8]), 1, 1, 1, 256, None), -6),
+    # dit_state_merge(o, lse, B, S_q, H, D, P, out, lse_out, qo, n_qb, imp, ws, wsb, st)
+    (lambda L: L.dit_state_merge(1, 1, 1, 8, 1, 64, 0, 1, 1, None, 0, None, None, 0, None), -2),
+    (lambda L: L.dit_state_merge(1, None, 1, 8, 1, 64, 2, 1, 1, None, 0, None, None, 0, None), -1),
     # 8M rows x 40 heads x 16 threads per row-head: more work-items than one dispatch can count
-    (lambda L: L.dit_state_merge(1, 1, 1, 8_000_000, 40, 128, 2, 1, 1, None), -2),
+    (lambda L: L.dit_state_merge(1, 1, 1, 8_000_000, 40, 128, 2, 1, 1, None, 0, None, None, 0, None), -2),
+    # importance in the merge: offsets checked, workspace required and large enough
+    (lambda L: L.dit_state_merge(1, 1, 1, 8, 1, 64, 2, 1, 1, None, 1, 1, 1, 1 << 20, None), -1),
+    (lambda L: L.dit_state_merge(1, 1, 1, 8, 1, 64, 2, 1, 1, _i32([0, 4, 4, 8]), 3, 1, 1, 1 << 20, None), -3),
+    (lambda L: L.dit_state_merge(1, 1, 1, 8, 1, 64, 2, 1, 1, _i32([0, 8]), 1, 1, None, 0, None), -6),
+    (lambda L: L.dit_state_merge(1, 1, 1, 8, 1, 64, 2, 1, 1, _i32([0, 8]), 1, 1, 1, 256, None), -6),
     # dit_state_merge_masked(o, lse, B, S_q, H, D, P, qo, n_qb, sel, extra_o, extra_lse, out, lse_out, st)
     (lambda L: L.dit_state_merge_masked(1, 1, 1, 8, 1, 64, 2, _i32([0, 8]), 1, _u8([1, 2]), None, None, 1, 1, None), -4),
     (lambda L: L.dit_state_merge_masked(1, 1, 1, 8, 1, 64, 2, _i32([0, 9]), 1, _u8([1, 0]), None, None, 1, 1, None), -3),

@@ -32,8 +32,8 @@ class Bufs:
         P, n_qb, S_q, H, D = w.P, w.n_qb, w.S_q, w.H, w.D
         dt = torch.uint8 if fp8 else torch.bfloat16
         self.cache_o = _sentinel(torch.empty((P, 1, S_q, H, D), dtype=dt, device="cuda"))
-        self.cache_scale = _sentinel(torch.empty((P, 1, H, S_q), dtype=torch.float32, device="cuda"))
-        self.cache_lse = _sentinel(torch.empty((P, 1, H, S_q), dtype=torch.float32, device="cuda"))
+        self.cache_scale = _sentinel(torch.empty((P, 1, S_q, H), dtype=torch.float32, device="cuda"))
+        self.cache_lse = _sentinel(torch.empty((P, 1, S_q, H), dtype=torch.float32, device="cuda"))
         self.out = _sentinel(torch.empty((1, S_q, H, D), dtype=torch.bfloat16, device="cuda"))
         self.lse = _sentinel(torch.empty((1, H, S_q), dtype=torch.float32, device="cuda"))
         self.imp = _sentinel(torch.empty((1, n_qb, P), dtype=torch.float32, device="cuda"))
@@ -41,7 +41,7 @@ class Bufs:
         nb = api.workspace_bytes(1, S_q, H, D, n_qb, P)
         self.ws = _sentinel(torch.empty(max(nb, 4) // 4, dtype=torch.float32, device="cuda"))
         self.comp_o = _sentinel(torch.empty((1, 1, S_q, H, D), dtype=torch.bfloat16, device="cuda"))
-        self.comp_l = _sentinel(torch.empty((1, 1, H, S_q), dtype=torch.float32, device="cuda"))
+        self.comp_l = _sentinel(torch.empty((1, 1, S_q, H), dtype=torch.float32, device="cuda"))
 
     def snapshot(self):
         torch.cuda.synchronize()

@@ -58,10 +58,10 @@ class Fp8Run(PT.GpuRun):
         """Decoded cache [P, n, H, D] (codes * scale) and the scales [P, H, n]."""
         idx = torch.as_tensor(rows, device="cuda")
         codes = self.sa.cache_o[:, 0][:, idx].cpu().numpy()
-        s = self.sa.cache_scale[:, 0][:, :, idx].double().cpu().numpy()
+        s = self.sa.cache_scale[:, 0][:, idx, :].double().cpu().numpy()     # [P, n, H]
         vals = oracle.decode_fp8_e4m3(codes)
         assert np.isfinite(vals).all(), "NaN code in the cache"
-        return vals * np.transpose(s, (0, 2, 1))[..., None], s
+        return vals * s[..., None], np.ascontiguousarray(np.transpose(s, (0, 2, 1)))
 
 
 def state_bound(O_exact):

@@ -30,7 +30,7 @@ def test_group_compose_then_continue_at_group_level():
     # composed planes against the oracle's composition of its stored states
     cO, cL = oracle.compose_states(o.cache.stored_O, o.cache.stored_lse, go)
     gO = PT.bf16_to_f64(sa2.cache_o[:, 0])
-    gL = sa2.cache_lse[:, 0].double().cpu().numpy()
+    gL = np.transpose(sa2.cache_lse[:, 0].double().cpu().numpy(), (0, 2, 1))   # [G, H, S] like the oracle
     PT.assert_rows_close(gO, cO, "composed planes")
     assert np.linalg.norm(gO - cO) / np.linalg.norm(cO) <= PT.O_REL_FRO_TOL
     assert np.abs(gL - cL).max() <= PT.LSE_ABS_TOL
@@ -62,7 +62,7 @@ def test_compose_rejects_bad_offsets():
     for bad in ([0, 2, 3], [0, 2, 2, 4], [1, 4]):
         G = len(bad) - 1    # output buffers sized for the groups the offsets claim
         out_o = torch.empty((G, 1, 64, 1, 64), dtype=torch.bfloat16, device="cuda")
-        out_l = torch.empty((G, 1, 1, 64), dtype=torch.float32, device="cuda")
+        out_l = torch.empty((G, 1, 64, 1), dtype=torch.float32, device="cuda")
         with pytest.raises(api.DitError):
             api.state_compose(sa.cache_o, sa.cache_lse, bad, out_o, out_l)
 
@@ -103,14 +103,14 @@ def test_masked_merge_selects_planes_per_block():
     qo = [0, 100, 300]
     torch.manual_seed(3)
     co = torch.randn((P, 1, S, H, D), device="cuda").to(torch.bfloat16)
-    cl = torch.randn((P, 1, H, S), device="cuda")
+    cl = torch.randn((P, 1, S, H), device="cuda")
     out = torch.empty((1, S, H, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, H, S), dtype=torch.float32, device="cuda")
     sel = np.array([[0, 0, 1, 0], [1, 0, 0, 0]], np.uint8)
     api.state_merge_masked(co, cl, qo, sel, out, lse)
     torch.cuda.synchronize()
     assert torch.equal(out[0, :100], co[2, 0, :100]) and torch.equal(out[0, 100:], co[0, 0, 100:])
-    assert torch.allclose(lse[0, :, :100], cl[2, 0, :, :100]) and torch.allclose(lse[0, :, 100:], cl[0, 0, :, 100:])
+    assert torch.allclose(lse[0, :, :100], cl[2, 0, :100].T) and torch.allclose(lse[0, :, 100:], cl[0, 0, 100:].T)
     api.state_merge_masked(co, cl, qo, np.zeros_like(sel), out, lse)
     torch.cuda.synchronize()
     assert (out.float() == 0).all() and torch.isneginf(lse).all()

@@ -259,14 +259,18 @@ def test_split_entry_points_match_one_call():
     dl = torch.empty_like(a.delta)
     ws = torch.empty_like(a.workspace)
     api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, m, co, cl, local_part=w.local_part,
-                            delta_partials=ws)
-    api.state_merge(co, cl, out, lse)
-    api.importance(cl, lse, w.q_offsets, imp)
+                            workspace=ws)
+    api.state_merge(co, cl, out, lse, q_offsets=w.q_offsets, importance_out=imp, workspace=ws)
     api.local_change_finalize(ws, 1, w.S_q, w.H, w.D, w.q_offsets, dl)
     torch.cuda.synchronize()
     assert torch.equal(out, a.out) and torch.equal(lse, a.lse)
     assert torch.equal(co, a.cache_o) and torch.equal(cl, a.cache_lse)
     assert torch.equal(imp, a.importance) and torch.equal(dl, a.delta)
+    # the second pass over the stored lse planes gives the same importance up to fp32 rounding
+    imp2 = torch.empty_like(imp)
+    api.importance(cl, lse, w.q_offsets, imp2)
+    torch.cuda.synchronize()
+    assert (imp2 - imp).abs().max().item() <= 1e-6
 
 
 def test_tile_sum_bound_and_maximum_jumps():

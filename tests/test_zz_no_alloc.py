@@ -49,7 +49,13 @@ def _one_case(w, mask_seed):
         outs[name] = (out, lse, imp, dl, co, cl)
     a, b = outs["workspace"], outs["noalloc"]
     for x, y, what in zip(a, b, ("out", "lse", "importance", "delta", "cache_o", "cache_lse")):
-        assert torch.equal(x, y), what
+        if what == "importance":
+            # the no-alloc call takes the importance in a second pass over the stored lse
+            # planes (no partials to keep); the other call inside the merge: same sums in
+            # another order
+            assert (x - y).abs().max().item() <= 1e-6, what
+        else:
+            assert torch.equal(x, y), what
     assert torch.isfinite(a[3]).all() and torch.isfinite(a[2]).all()
     _log(f"{w.name} S_q={w.S_q} H={w.H}: no-alloc step equal to the workspace step "
          f"(delta {a[3][0, :3].tolist()})")
@@ -82,15 +88,20 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
     is DIT_ERR_WORKSPACE (the fake device pointers are never dereferenced)."""
     L = _lib.lib()
     H, D = 40, 128
+
+    def scratch_need(S_q, n_qb=1):
+        # schedule counters (256 B), then one (num, den) pair per (128-row query tile, head)
+        return 256 + ((S_q + 127) // 128 + n_qb) * H * 8
+
     S_q = 600_000                                     # (4688 tiles + 1) * 40 * 8 B > 1 MiB
-    assert L.dit_attn_workspace_bytes(1, S_q, H, D, 1, 2) > (1 << 20)
+    assert scratch_need(S_q) > (1 << 20)
     i32 = lambda s: (ctypes.c_int32 * len(s))(*s)
     u8 = lambda s: (ctypes.c_uint8 * len(s))(*s)
     rc = L.dit_attn_partitioned_noalloc(16, 16, 16, 1, S_q, 64, H, D, i32([0, S_q]), 1, i32([0, 32, 64]), 2,
                                         i32([0]), u8([1, 0]), None, 16, 16, 16, 16, 0.0, None, 16, None)
     assert rc == -6
     S_q = 200_000                                     # fits: rejected later, for the NULL q
-    assert L.dit_attn_workspace_bytes(1, S_q, H, D, 1, 2) <= (1 << 20)
+    assert scratch_need(S_q) <= (1 << 20)
     rc = L.dit_attn_partitioned_noalloc(None, 16, 16, 1, S_q, 64, H, D, i32([0, S_q]), 1, i32([0, 32, 64]), 2,
                                         i32([0]), u8([1, 0]), None, 16, 16, 16, 16, 0.0, None, 16, None)
     assert rc == -1
