@@ -104,6 +104,133 @@ def summarize_profile(db_path: str) -> str:
         d = np.array(durs, dtype=np.float64) / 1e3
         lines.append(f"{short[:48]:<48} {f'{gx},{gy},{gz}':>22} {wx:>4} {vg:>5} {ag:>5} {lds:>6} {len(d):>5} "
                      f"{d.mean():>11.2f} {d.min():>11.2f} {d.max():>11.2f}")
+    # two-stream steps: how long each masked merge ran alongside an attention dispatch
+    try:
+        disp = con.execute("select name, start, end from kernels order by start").fetchall()
+    except Exception:
+        disp = []
+    attn = [(a, b) for n, a, b in disp if "partition_attention_kernel" in n]
+    masked = [(a, b) for n, a, b in disp if "state_merge_masked_kernel" in n]
+    if attn and masked:
+        lines.append("")
+        lines.append("# masked merges (two-stream step) against the attention dispatches they overlap (us):")
+        lines.append(f"{'merge start':>12} {'merge dur':>10} {'overlap':>10} {'attn start':>12} {'attn dur':>10}")
+        t0 = min(a for a, _ in attn + masked)
+        for a, b in masked:
+            best = max(attn, key=lambda ab: max(0, min(b, ab[1]) - max(a, ab[0])))
+            ov = max(0, min(b, best[1]) - max(a, best[0]))
+            lines.append(f"{(a - t0) / 1e3:>12.1f} {(b - a) / 1e3:>10.1f} {ov / 1e3:>10.1f} {(best[0] - t0) / 1e3:>12.1f} "
+                         f"{(best[1] - best[0]) / 1e3:>10.1f}")
+    return "\n".join(lines)
+
+
+def read_pmc(dirpath: str) -> dict:
+    """Per (kernel, grid size) from a rocprofv3 --pmc CSV run: {counter: [value per dispatch]}
+    and the dispatch durations in ns."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {dirpath}")
+    out = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                name = row["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                key = (name, int(row["Grid_Size"]))
+                d = out.setdefault(key, {"dispatch": {}})
+                disp = d["dispatch"].setdefault(row["Dispatch_Id"], {})
+                disp[row["Counter_Name"]] = disp.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+                disp["_ns"] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+    return out
+
+
+def pmc_mean(rec: dict, counter: str) -> float:
+    vals = [d[counter] for d in rec["dispatch"].values() if counter in d]
+    return float(np.mean(vals)) if vals else float("nan")
+
+
+def summarize_pmc(workload: str, out_json: str, fetch_dir: str, write_dir: str, sq_dirs: list) -> str:
+    """HBM traffic per launch of every kernel of one workload's steps from FETCH_SIZE and
+    WRITE_SIZE runs, scaled by the same counters' reading for the 4 GiB device copy of the
+    bench (bytes known), plus the attention kernel's SQ-counter figures; writes the record the
+    bench reads (profiles/traffic_<workload>.json) and returns a text summary."""
+    from partitioned_state_reuse_amd import api
+    w = W.workload(workload)
+    mode = "anchor" if w.mode == "anchor" else "distance"
+    pl = api.Planner(w.n_qb, w.P, w.group_offsets, w.local_part, w.anchor_every or 0, w.recompute_groups, mode)
+    mask, _ = pl.next(1)
+    pl.close()
+    qt = [math.ceil(n / 128) for n in np.diff(w.q_offsets)]
+    attn_grid = w.H * int(sum(qt[i] for i in range(w.n_qb) for p in range(w.P) if mask[i, p])) * 256
+    merge_grid = math.ceil(w.S_q * w.H / 16) * 256
+    fetch, write = read_pmc(fetch_dir), read_pmc(write_dir)
+    copy_bytes = 1 << 32
+    cf = [v for (n, g), v in fetch.items() if "copyBuffer" in n]
+    cw = [v for (n, g), v in write.items() if "copyBuffer" in n]
+    fetch_copy, write_copy = pmc_mean(cf[0], "FETCH_SIZE"), pmc_mean(cw[0], "WRITE_SIZE")
+    rf, wf = copy_bytes / (fetch_copy * 1024), copy_bytes / (write_copy * 1024)
+    kernels = {}
+    for (name, grid), rec in fetch.items():
+        if "copyBuffer" in name or (name, grid) not in write:
+            continue
+        if not ((name.startswith("dit::partition_attention") and grid == attn_grid) or
+                (name.startswith("dit::state_merge") and grid in (merge_grid, merge_grid // 2)) or
+                name in ("dit::delta_finalize_kernel", "dit::importance_finalize_kernel", "dit::importance_kernel")):
+            continue
+        fk, wk = pmc_mean(rec, "FETCH_SIZE"), pmc_mean(write[(name, grid)], "WRITE_SIZE")
+        kernels[f"{name}"] = {"grid_threads": grid, "fetch_kib": fk, "write_kib": wk,
+                              "hbm_read_bytes": fk * 1024 * rf, "hbm_write_bytes": wk * 1024 * wf,
+                              "traffic_bytes": fk * 1024 * rf + wk * 1024 * wf,
+                              "dispatches": len(rec["dispatch"])}
+    rec = {"workload": workload, "source_sha256": kernel_source_sha256(),
+           "command": f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv -- python3 -u bench.py "
+                      f"--steps 2 --warmup 0 --no-cpu-baseline (then the same with WRITE_SIZE)",
+           "calibration": {"kernel": "__amd_rocclr_copyBuffer (the 4 GiB device copy in bench.py)",
+                           "bytes_read": copy_bytes, "bytes_written": copy_bytes, "fetch_kib": fetch_copy,
+                           "write_kib": write_copy, "read_factor": rf, "write_factor": wf},
+           "kernels": kernels}
+    lines = [f"# HBM traffic per launch, {workload} (attention grid {attn_grid} threads, merge grid {merge_grid})",
+             f"# calibration: the 4 GiB device copy reads FETCH_SIZE {fetch_copy:.0f} KiB and WRITE_SIZE {write_copy:.0f} KiB"
+             f" -> read factor {rf:.4f}, write factor {wf:.4f}"]
+    for n, k in kernels.items():
+        lines.append(f"#   {n:<46} FETCH {k['fetch_kib']:>12.0f} KiB x {rf:.4f} = {k['hbm_read_bytes'] / 1e9:8.3f} GB read, "
+                     f"WRITE {k['write_kib']:>12.0f} KiB x {wf:.4f} = {k['hbm_write_bytes'] / 1e9:8.3f} GB written")
+    if sq_dirs:
+        sq = {}
+        for dpath in sq_dirs:
+            for key, r in read_pmc(dpath).items():
+                if key[0] == "dit::partition_attention_kernel<128, false>" and key[1] == attn_grid:
+                    for c in {c for d in r["dispatch"].values() for c in d if not c.startswith("_")}:
+                        sq[c] = pmc_mean(r, c)
+                    sq["_ns"] = pmc_mean(r, "_ns")
+        clocks = sq["GRBM_GUI_ACTIVE"] / 8
+        ghz = clocks / sq["_ns"]
+        busy = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * clocks)
+        counters = {"kernel": "dit::partition_attention_kernel<128, false>", "clock_ghz_under_load": round(ghz, 3),
+                    "mfma_busy_frac": round(busy, 4), "peak_tflops_at_that_clock": round(PEAK_BF16_TFLOPS * ghz / 2.4, 1),
+                    "commands": "rocprofv3 --pmc <SQ counters> -- python3 -u bench.py --steps 2 --warmup 0 "
+                                "--no-cpu-baseline (two passes)"}
+        if "SQ_WAIT_ANY" in sq:
+            counters["waves_waiting_frac"] = round(sq["SQ_WAIT_ANY"] / sq["SQ_WAVE_CYCLES"], 4)
+        if "SQ_LDS_IDX_ACTIVE" in sq:
+            counters["lds_indexed_active_frac"] = round(sq["SQ_LDS_IDX_ACTIVE"] / (256 * clocks), 4)
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in sq:
+            counters["mfma_valu_coexec_frac"] = round(sq["SQ_VALU_MFMA_COEXEC_CYCLES"] / (1024 * clocks), 4)
+        if "SQ_INSTS_VALU" in sq:
+            counters["valu_instructions_per_mfma"] = round(sq["SQ_INSTS_VALU"] / sq["SQ_INSTS_MFMA"], 3)
+        rec["attention_counters"] = counters
+        lines.append(f"# SQ counters of dit::partition_attention_kernel<128, false> (mean over {attn_grid}-thread dispatches):")
+        for c in sorted(k for k in sq if not k.startswith("_")):
+            lines.append(f"#   {c:<28} {sq[c]:.4e}")
+        lines.append(f"#   dispatch duration under the counters {sq['_ns'] / 1e6:.2f} ms; GRBM_GUI_ACTIVE / 8 XCDs = "
+                     f"{clocks:.4e} clocks -> {ghz:.2f} GHz; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x clocks)"
+                     f" = {busy:.1%}")
+        for k, v in counters.items():
+            if k.endswith("_frac") or k.endswith("_per_mfma"):
+                lines.append(f"#   {k} {v}")
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
     return "\n".join(lines)
 
 
@@ -180,10 +307,28 @@ def run_trajectory(args, w: "W.Workload") -> dict:
     }
 
 
-def evict_cache(buf) -> None:
-    """Overwrite a buffer larger than the 256 MB Infinity Cache (MALL) so that a following
-    kernel reads its inputs from HBM, not from data the previous kernel left in the MALL."""
-    buf.fill_(1)
+def cold_ms(launch, copies, reps: int) -> float:
+    """Median duration (HIP events on the launch stream) of `launch(copy)` over `reps` launches
+    that rotate over several copies of the same state cache: each launch reads planes last
+    touched one or more whole merges earlier (at least 0.8 GB of other traffic, beyond the
+    256 MB Infinity Cache, the MALL), and no overwrite is needed to empty the MALL, which
+    would leave dirty lines to be written back during the timed launch."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for c in copies:
+        launch(c)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        launch(copies[i % len(copies)])
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
+def cache_copies(tensors, n: int):
+    """The cache tensors plus n - 1 clones (for cold_ms)."""
+    return [tuple(tensors)] + [tuple(t.clone() for t in tensors) for _ in range(n - 1)]
 
 
 def oracle_leg(w: W.Workload, X: "W.StepInputs", Xp: "W.StepInputs", mask: np.ndarray, rows: np.ndarray,
@@ -247,7 +392,7 @@ def oracle_leg(w: W.Workload, X: "W.StepInputs", Xp: "W.StepInputs", mask: np.nd
     return out, parity
 
 
-def layer_bench(w: W.Workload, args, dev, evict_buf, extras: bool) -> dict:
+def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
     """Time the selective step of one single-step layer and its two kernels."""
     import torch
     from partitioned_state_reuse_amd import api
@@ -309,22 +454,24 @@ def layer_bench(w: W.Workload, args, dev, evict_buf, extras: bool) -> dict:
     gpu_out = W.to_f64(sa.out[0, ridx].view(torch.int16).cpu().numpy().view(np.uint16))
     gpu_lse = sa.lse[0][:, ridx].double().cpu().numpy()
 
-    # the merge alone, each launch after an overwrite of the Infinity Cache
-    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in mev:
-        evict_cache(evict_buf)
-        e[0].record(stream)
-        api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    merge_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
+    # the merge alone on a cold cache (rotating over copies of the cache); the importance
+    # variant of anchor steps on the same copies
+    copies = cache_copies((sa.cache_o, sa.cache_lse), 2 if w.S_q * w.H * w.P * 260 > 4e9 else 3)
+    merge_ms = cold_ms(lambda c: api.state_merge(c[0], c[1], sa.out, sa.lse, stream=stream), copies,
+                       max(args.steps, 6))
+    imp = torch.empty((1, w.n_qb, w.P), dtype=torch.float32, device=dev)
+    anchor_merge_ms = cold_ms(lambda c: api.state_merge(c[0], c[1], sa.out, sa.lse, q_offsets=w.q_offsets,
+                                                        importance_out=imp, workspace=sa.workspace, stream=stream),
+                              copies, max(args.steps, 6))
+    del copies
 
     flop = attn_flop(w, mask)
     mbytes = merge_bytes(w)
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
     merge_gbs = mbytes / (merge_ms * 1e-3) / 1e9
     log(f"[bench] {w.name}: step {ms_step:.3f} ms  attention {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s)  "
-        f"merge {merge_ms:.3f} ms after MALL eviction ({merge_gbs:.0f} GB/s; in the step {merge_in_step_ms:.3f} ms)  "
+        f"merge {merge_ms:.3f} ms cold ({merge_gbs:.0f} GB/s; in the step {merge_in_step_ms:.3f} ms; with importance "
+        f"{anchor_merge_ms:.3f} ms)  "
         f"finalize {fin_ms:.4f} ms")
     traffic = measured_traffic(w.name)
     attn_counters = measured_counters(w.name)
@@ -348,14 +495,17 @@ def layer_bench(w: W.Workload, args, dev, evict_buf, extras: bool) -> dict:
                            "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
                            "traffic": traffic.get("dit::" + merge_kernel),
                            "kernel": merge_kernel, "ms": round(merge_ms, 4), "ms_in_step": round(merge_in_step_ms, 4),
-                           "algorithmic_bytes": mbytes, "timing": "each launch after a 1 GiB overwrite of the MALL"},
+                           "algorithmic_bytes": mbytes,
+                           "timing": "median over launches rotating over copies of the cache (cold MALL)",
+                           "anchor_ms": round(anchor_merge_ms, 4),
+                           "anchor_what": "the same merge with the importance partials and their fixed-order finish"},
         "local_change_finalize_ms": round(fin_ms, 5),
     }
     ctx = {"X": X, "Xp": Xp, "mask": mask, "rows": rows, "gpu_out": gpu_out, "gpu_lse": gpu_lse,
            "q": q, "k": k, "v": v, "sa": sa, "planner": planner, "flop": flop, "ms_step": ms_step,
            "merge_ms": merge_ms}
     if extras:
-        res.update(layer_extras(w, args, dev, ctx, evict_buf))
+        res.update(layer_extras(w, args, dev, ctx))
     else:
         ov_ms = overlapped_step_ms(args, ctx)
         log(f"[bench] {w.name}: overlapped step {ov_ms:.3f} ms (plain {ms_step:.3f})")
@@ -382,26 +532,16 @@ def overlapped_step_ms(args, ctx) -> float:
     return (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
 
 
-def layer_extras(w: W.Workload, args, dev, ctx, evict_buf) -> dict:
+def layer_extras(w: W.Workload, args, dev, ctx) -> dict:
     """Importance, planner and enqueue costs, the two-stream step, group compose and the
     compressed cache on the same layer."""
     import torch
     from partitioned_state_reuse_amd import api
     q, k, v, sa, planner, flop, mask = ctx["q"], ctx["k"], ctx["v"], ctx["sa"], ctx["planner"], ctx["flop"], ctx["mask"]
     stream = torch.cuda.current_stream()
-    # a5 importance (anchor steps): inside the merge (partials + a fixed-order finish), timed
-    # like the plain merge after an overwrite of the MALL, and the second pass over the stored
-    # lse planes that callers without a workspace use
+    # a5 importance by the second pass over the stored lse planes (callers without a
+    # workspace; anchor steps otherwise take it inside the merge, timed with the merge)
     imp = torch.empty((1, w.n_qb, w.P), dtype=torch.float32, device=dev)
-    aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in aev:
-        evict_cache(evict_buf)
-        e[0].record(stream)
-        api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, q_offsets=w.q_offsets, importance_out=imp,
-                        workspace=sa.workspace, stream=stream)
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    anchor_merge_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in aev]))
     api.importance(sa.cache_lse, sa.lse, w.q_offsets, imp, stream=stream)
     i0, i1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     i0.record(stream)
@@ -422,18 +562,8 @@ def layer_extras(w: W.Workload, args, dev, ctx, evict_buf) -> dict:
                                 local_part=w.local_part, stream=stream)
     enqueue_us = (time.perf_counter() - t0) / 3 * 1e6
     torch.cuda.synchronize()
-    # the same attention launch without a workspace: every workgroup's item fixed at launch
-    # (no balancing across the XCDs, no local-change partials)
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    for _ in range(args.steps):
-        api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse, stream=stream)
-    s1.record(stream)
-    torch.cuda.synchronize()
-    static_ms = s0.elapsed_time(s1) / max(args.steps, 1)
-    log(f"[bench] attention without a workspace (static placement) {static_ms:.3f} ms")
-    log(f"[bench] merge with importance {anchor_merge_ms:.3f} ms (plain {ctx['merge_ms']:.3f}); second-pass importance "
-        f"{imp_ms:.3f} ms, planner {planner_us:.1f} us/call, attention enqueue {enqueue_us:.1f} us")
+    log(f"[bench] second-pass importance {imp_ms:.3f} ms, planner {planner_us:.1f} us/call, attention enqueue "
+        f"{enqueue_us:.1f} us")
 
     ov_ms = overlapped_step_ms(args, ctx)
     # dynamic group compose of the P cached states into the groups
@@ -484,14 +614,10 @@ def layer_extras(w: W.Workload, args, dev, ctx, evict_buf) -> dict:
     torch.cuda.synchronize()
     fp8_ms = (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
     fp8_attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev8]))
-    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in mev:
-        evict_cache(evict_buf)
-        e[0].record(stream)
-        api.state_merge_fp8(sa8.cache_o, sa8.cache_scale, sa8.cache_lse, sa8.out, sa8.lse, stream=stream)
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    fp8_merge_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
+    copies = cache_copies((sa8.cache_o, sa8.cache_scale, sa8.cache_lse), 2)
+    fp8_merge_ms = cold_ms(lambda c: api.state_merge_fp8(c[0], c[1], c[2], sa8.out, sa8.lse, stream=stream), copies,
+                           max(args.steps, 6))
+    del copies
     # per row-head: P planes of D code bytes + scale + lse read, bf16 output + lse written
     fp8_bytes = float(w.S_q * w.H * (w.P * (w.D + 8) + 2 * w.D + 4))
     del sa8
@@ -510,11 +636,7 @@ def layer_extras(w: W.Workload, args, dev, ctx, evict_buf) -> dict:
                       "merge_frac": round(fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                       "merge_algorithmic_bytes": fp8_bytes,
                       "value": round(flop / (fp8_ms * 1e-3) / 1e12, 2)},
-        "anchor_merge": {"ms": round(anchor_merge_ms, 4), "plain_merge_ms": round(ctx["merge_ms"], 4),
-                         "gbs": round(merge_bytes(w) / (anchor_merge_ms * 1e-3) / 1e9, 1),
-                         "what": "merge with the importance partials and their fixed-order finish (two launches)"},
         "importance_second_pass_ms": round(imp_ms, 4),
-        "attention_static_placement_ms": round(static_ms, 4),
         "planner_us_per_step": round(planner_us, 2),
         "attention_enqueue_us": round(enqueue_us, 2),
     }
@@ -523,6 +645,10 @@ def layer_extras(w: W.Workload, args, dev, ctx, evict_buf) -> dict:
 def main() -> int:
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profile":
         print(summarize_profile(sys.argv[2]))
+        return 0
+    if len(sys.argv) >= 6 and sys.argv[1] == "--summarize-pmc":
+        # --summarize-pmc <workload> <out.json> <FETCH_SIZE dir> <WRITE_SIZE dir> [<SQ dir> ...]
+        print(summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6:]))
         return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -547,8 +673,7 @@ def main() -> int:
     if w.mode == "wdelta":
         print(json.dumps(run_trajectory(args, w)), flush=True)
         return 0
-    evict_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    layer, ctx = layer_bench(w, args, dev, evict_buf, extras=(w.name == "video720p"))
+    layer, ctx = layer_bench(w, args, dev, extras=(w.name == "video720p"))
 
     # plain device copy of 4 GiB as the achievable-bandwidth reference (and PMC calibration)
     stream = torch.cuda.current_stream()
@@ -569,10 +694,9 @@ def main() -> int:
     share = None
     if w.name == "video720p" and not args.no_share32:
         ws = W.workload("share32")
-        share, sctx = layer_bench(ws, args, dev, evict_buf, extras=False)
+        share, sctx = layer_bench(ws, args, dev, extras=False)
         share["metric"] = "recomputed-attn TFLOP/s + merge GB/s, one GPU's share of a 32-way split of 75.6k tokens"
         share["unit"] = "TFLOP/s"
-    del evict_buf
     result = {
         "metric": "recomputed-attn TFLOP/s + merge GB/s at 75.6k tokens, % of MFMA/HBM peak",
         "value": layer["value"],

@@ -89,10 +89,9 @@ typedef enum {
 const char *dit_status_string(int status);
 
 /* Bytes of device workspace dit_attn_partitioned needs for these sizes, for any split into
- * n_qb query blocks: 256 bytes of schedule counters of the attention launch, the
- * local-change partial sums of the attention kernel, then the importance partials of the
- * merge (P floats per merge workgroup).  The split calls take the same workspace.  Returns
- * 0 if the sizes are invalid. */
+ * n_qb query blocks: the local-change partial sums of the attention kernel, then the
+ * importance partials of the merge (P floats per merge workgroup).  The split calls take the
+ * same workspace.  Returns 0 if the sizes are invalid. */
 size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P);
 
 /*
@@ -111,11 +110,9 @@ size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P);
  *                      a workspace; with cache_valid given the local slots must be valid.
  *   workspace          device, >= dit_attn_workspace_bytes(...) when delta_out or
  *                      importance_out is given, else may be NULL.  Contents on entry are
- *                      ignored.  When given, the attention launch is balanced across the
- *                      XCDs (see dit_partition_attention), and the importance is computed
- *                      inside the merge (partial sums per merge workgroup, finished in a
- *                      fixed order).  Calls that share a workspace must not run at the same
- *                      time.
+ *                      ignored.  The importance is computed inside the merge (partial sums
+ *                      per merge workgroup, finished in a fixed order).  Calls that share a
+ *                      workspace must not run at the same time.
  */
 int dit_attn_partitioned(const void *q, const void *k, const void *v,
                          int B, int S_q, int S_kv, int H, int D,
@@ -140,16 +137,14 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v,
  * memory, held until the process ends; its address is looked up once per device, on the
  * first call that needs it with that device current).  The call allocates nothing: no
  * hipMalloc, hipFree or allocating library routine.
- *   - delta_out given and 256 + B * (ceil(S_q / 128) + n_qb) * H * 8 bytes (the schedule
- *     counters and the local-change partials) above DIT_SCRATCH_BYTES: DIT_ERR_WORKSPACE
- *     (e.g. B = 1, H = 40 allows about 3,270 query tiles of 128 rows plus blocks, S_q up to
- *     ~410,000 rows).
- *   - The array holds the attention launch's schedule counters (cleared by each call with a
- *     small kernel, not a memset) and the local-change partial sums; the importance, when
- *     asked for, is taken in a second pass over the stored lse planes (no partials kept).
- *     The array keeps the last call's contents; every other entry a call reads is written by
- *     the same call.  Calls that overlap on one GPU (on different streams, or from different
- *     threads) share the array and race: serialise them.
+ *   - delta_out given and B * (ceil(S_q / 128) + n_qb) * H * 8 bytes (the local-change
+ *     partials) above DIT_SCRATCH_BYTES: DIT_ERR_WORKSPACE (e.g. B = 1, H = 40 allows about
+ *     3,270 query tiles of 128 rows plus blocks, S_q up to ~410,000 rows).
+ *   - The array holds the local-change partial sums; the importance, when asked for, is
+ *     taken in a second pass over the stored lse planes (no partials kept).  The array keeps
+ *     the last call's contents; every entry a call reads is written by the same call, so
+ *     nothing needs clearing.  Calls that overlap on one GPU (on different streams, or from
+ *     different threads) share the array and race: serialise them.
  *   - Unlike the other calls this one keeps state across calls (the per-device address).
  */
 int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v,
@@ -177,16 +172,13 @@ int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v,
  *                      read it), and so is a local slot marked invalid when the local-change
  *                      partials are written.
  *   workspace          device or NULL, of workspace_bytes >= dit_attn_workspace_bytes(...).
- *                      When given, the launch is balanced across the XCDs (the first 256
- *                      bytes hold the counters through which workgroups claim the last fifth
- *                      of each XCD's items; they are cleared by the call itself); without
- *                      it every workgroup's item is fixed at launch.  When given together
- *                      with local_part, the kernel also writes, per (query tile, head) of
- *                      each block's local partition, the sums sum (O_new - O_old)^2 and
- *                      sum O_old^2 over the tile's rows and D, where O_old is the slot's
- *                      content before this call and O_new the value written; finish them
- *                      with dit_local_change_finalize on the same workspace.  Calls that
- *                      share a workspace must not run at the same time.
+ *                      When given (with local_part, else DIT_ERR_NULL), the kernel also
+ *                      writes, per (query tile, head) of each block's local partition, the
+ *                      sums sum (O_new - O_old)^2 and sum O_old^2 over the tile's rows and D,
+ *                      where O_old is the slot's content before this call and O_new the value
+ *                      written; finish them with dit_local_change_finalize on the same
+ *                      workspace.  Calls that share a workspace must not run at the same
+ *                      time.
  */
 int dit_partition_attention(const void *q, const void *k, const void *v,
                             int B, int S_q, int S_kv, int H, int D,

@@ -136,9 +136,8 @@ def attn_partitioned_noalloc(q, k, v, q_offsets, kv_offsets, recompute, cache_o,
 def partition_attention(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, *,
                         local_part=None, cache_valid=None, scale: float = 0.0, workspace=None,
                         stream=None) -> None:
-    """dit_partition_attention.  With a workspace the launch is balanced across the XCDs; with
-    local_part as well it also writes the local-change partial sums (finish them with
-    local_change_finalize)."""
+    """dit_partition_attention.  With a workspace (and local_part) it also writes the
+    local-change partial sums (finish them with local_change_finalize)."""
     (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
     n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
     wp, ws_bytes = _ws(workspace, "workspace")
@@ -336,8 +335,8 @@ class SelectiveAttention:
                            self.partial_lse, stream=side_stream)
         do_delta = want_delta and all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
         partition_attention(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
-                            local_part=self.local_part if do_delta else None, cache_valid=self.valid, scale=scale,
-                            workspace=self.workspace, stream=main)
+                            local_part=self.local_part, cache_valid=self.valid, scale=scale,
+                            workspace=self.workspace if do_delta else None, stream=main)
         done = torch.cuda.Event()
         done.record(side_stream)
         main.wait_event(done)
@@ -384,8 +383,9 @@ class SelectiveAttention:
         do_delta = want_delta and local_valid
         if self.cache_format == "fp8":
             partition_attention_fp8(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o,
-                                    self.cache_scale, self.cache_lse, local_part=self.local_part if do_delta else None,
-                                    cache_valid=self.valid, scale=scale, workspace=self.workspace, stream=stream)
+                                    self.cache_scale, self.cache_lse, local_part=self.local_part,
+                                    cache_valid=self.valid, scale=scale,
+                                    workspace=self.workspace if do_delta else None, stream=stream)
             state_merge_fp8(self.cache_o, self.cache_scale, self.cache_lse, self.out, self.lse,
                             q_offsets=self.q_offsets, importance_out=self.importance if want_importance else None,
                             workspace=self.workspace, stream=stream)
@@ -397,6 +397,7 @@ class SelectiveAttention:
         attn_partitioned(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
                          self.out, self.lse, local_part=self.local_part, cache_valid=self.valid, scale=scale,
                          importance_out=self.importance if want_importance else None,
-                         delta_out=self.delta if do_delta else None, workspace=self.workspace, stream=stream)
+                         delta_out=self.delta if do_delta else None,
+                         workspace=self.workspace if (do_delta or want_importance) else None, stream=stream)
         self.valid |= recompute
         return do_delta

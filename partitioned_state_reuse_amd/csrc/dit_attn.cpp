@@ -63,22 +63,15 @@ void fill_blocks(BlockDesc &bd, const int32_t *q_offsets, int n_qb) {
   bd.n_tiles = bd.tile_prefix[n_qb];
 }
 
-// Workspace layout: the attention launch's schedule counters (kSchedBytes), the local-change
-// partial sums of the attention kernel, then (from the next 256-byte boundary) the
-// importance partials of the merge.
+// Workspace layout: the local-change partial sums of the attention kernel, then (from the
+// next 256-byte boundary) the importance partials of the merge.
 size_t delta_ws_bytes(int B, int S_q, int H, int n_qb) {
   // upper bound on the tile count of any split into n_qb blocks
   const int64_t tiles = (int64_t)(S_q + dit::kBlockM - 1) / dit::kBlockM + n_qb;
   return (size_t)B * (size_t)tiles * (size_t)H * 2 * sizeof(float);
 }
 
-constexpr size_t kDeltaOffset = dit::kSchedBytes;
-
-size_t imp_ws_offset(int B, int S_q, int H, int n_qb) {
-  return (kDeltaOffset + delta_ws_bytes(B, S_q, H, n_qb) + 255) & ~(size_t)255;
-}
-
-float *delta_region(void *workspace) { return (float *)((char *)workspace + kDeltaOffset); }
+size_t imp_ws_offset(int B, int S_q, int H, int n_qb) { return (delta_ws_bytes(B, S_q, H, n_qb) + 255) & ~(size_t)255; }
 
 // Upper bound on the importance partials of any split into n_qb blocks: every merge variant
 // takes at least 16 row-heads per workgroup, and each block adds at most one partly filled
@@ -128,11 +121,10 @@ int build_attn(const void *q, const void *k, const void *v, int B, int S_q, int 
     for (int e = 0; e < n_qb * P; ++e)
       if (!recompute[e] && !cache_valid[e]) return DIT_ERR_CACHE_INVALID;
   }
-  if (workspace && workspace_bytes < dit::kSchedBytes) return DIT_ERR_WORKSPACE;
   if (want_delta) {
     if (!local_part) return DIT_ERR_NULL;
     if (!workspace) return DIT_ERR_WORKSPACE;
-    if (workspace_bytes < kDeltaOffset + delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
+    if (workspace_bytes < delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
     if (cache_valid)
       for (int i = 0; i < n_qb; ++i)
         if (!cache_valid[i * P + local_part[i]]) return DIT_ERR_CACHE_INVALID;
@@ -161,11 +153,9 @@ int build_attn(const void *q, const void *k, const void *v, int B, int S_q, int 
     desc.item_prefix[p + 1] = desc.item_prefix[p] + items;
   }
   desc.items_per_head = desc.item_prefix[P];
-  // one workgroup of kWaves * 64 threads per (batch, head, item), plus the spare workgroups
-  // of a balanced launch; a dispatch counts its work-items in 32 bits
+  // one workgroup of kWaves * 64 threads per (batch, head, item); a dispatch counts its
+  // work-items in 32 bits
   if ((int64_t)B * H * desc.items_per_head * (dit::kWaves * 64) > (int64_t)UINT32_MAX) return DIT_ERR_SHAPE;
-  if (dit::attention_launch_shape(desc, workspace != nullptr).workgroups * (dit::kWaves * 64) > (int64_t)UINT32_MAX)
-    return DIT_ERR_SHAPE;
   for (int i = 0; i < n_qb; ++i) desc.local_part[i] = (want_delta && local_part) ? local_part[i] : -1;
   return DIT_OK;
 }
@@ -199,7 +189,7 @@ int run_partitioned(const void *q, const void *k, const void *v, int B, int S_q,
       return st;
     hipStream_t s = as_stream(stream);
     if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse,
-                                        want_delta ? delta_region(workspace) : nullptr, (int *)workspace, desc,
+                                        want_delta ? (float *)workspace : nullptr, desc,
                                         scale_log2_of(softmax_scale, D), s) != hipSuccess)
       return DIT_ERR_HIP;
     if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, false, fuse ? &bd : nullptr, imp_part,
@@ -208,7 +198,7 @@ int run_partitioned(const void *q, const void *k, const void *v, int B, int S_q,
     if (importance_out && !fuse &&
         dit::launch_importance(cache_lse, lse, B, S_q, H, P, bd, importance_out, s) != hipSuccess)
       return DIT_ERR_HIP;
-    if (want_delta && dit::launch_delta_finalize(delta_region(workspace), B, H, bd, delta_out, s) != hipSuccess)
+    if (want_delta && dit::launch_delta_finalize((const float *)workspace, B, H, bd, delta_out, s) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
   } catch (...) {
@@ -250,13 +240,13 @@ int dit_partition_attention(const void *q, const void *k, const void *v, int B, 
                             size_t workspace_bytes, void *stream) {
   try {
     AttnDesc desc;
-    const bool want_delta = workspace != nullptr && local_part != nullptr;
+    const bool want_delta = workspace != nullptr;
     int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part,
                         recompute, cache_valid, cache_o, cache_lse, want_delta, workspace,
                         workspace_bytes, desc);
     if (st) return st;
     if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse,
-                                        want_delta ? delta_region(workspace) : nullptr, (int *)workspace, desc,
+                                        want_delta ? (float *)workspace : nullptr, desc,
                                         scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
@@ -273,12 +263,12 @@ int dit_partition_attention_fp8(const void *q, const void *k, const void *v, int
   try {
     if (!cache_scale) return DIT_ERR_NULL;
     AttnDesc desc;
-    const bool want_delta = workspace != nullptr && local_part != nullptr;
+    const bool want_delta = workspace != nullptr;
     int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
                         cache_valid, cache_q8, cache_lse, want_delta, workspace, workspace_bytes, desc);
     if (st) return st;
     if (dit::launch_partition_attention(D, true, q, k, v, cache_q8, cache_scale, cache_lse,
-                                        want_delta ? delta_region(workspace) : nullptr, (int *)workspace, desc,
+                                        want_delta ? (float *)workspace : nullptr, desc,
                                         scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
@@ -414,10 +404,10 @@ int dit_local_change_finalize(const void *workspace, size_t workspace_bytes, int
     int st = check_dims(B, S_q, 0, H, D);
     if (st) return st;
     if ((st = check_q_offsets(q_offsets, n_qb, S_q))) return st;
-    if (workspace_bytes < kDeltaOffset + delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
+    if (workspace_bytes < delta_ws_bytes(B, S_q, H, n_qb)) return DIT_ERR_WORKSPACE;
     BlockDesc bd;
     fill_blocks(bd, q_offsets, n_qb);
-    if (dit::launch_delta_finalize(delta_region((void *)workspace), B, H, bd, delta_out, as_stream(stream)) !=
+    if (dit::launch_delta_finalize((const float *)workspace, B, H, bd, delta_out, as_stream(stream)) !=
         hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
@@ -443,12 +433,15 @@ int dit_attn_partitioned_noalloc(const void *q, const void *k, const void *v, in
                                  void *cache_o, float *cache_lse, void *out, float *lse, float softmax_scale,
                                  float *importance_out, float *delta_out, void *stream) {
   try {
-    // the library's own device scratch stands in for the workspace: schedule counters and
-    // local-change partials (sizes beyond it are rejected by the workspace check,
-    // DIT_ERR_WORKSPACE); the importance is taken in a second pass, which needs none
+    // the library's own device scratch stands in for the workspace: the local-change partials
+    // (sizes beyond it are rejected by the workspace check, DIT_ERR_WORKSPACE); the importance
+    // is taken in a second pass, which needs none
     void *ws = nullptr;
-    if (dit::scratch_address(&ws) != hipSuccess) return DIT_ERR_HIP;
-    const size_t ws_bytes = dit::kScratchBytes;
+    size_t ws_bytes = 0;
+    if (delta_out != nullptr) {
+      if (dit::scratch_address(&ws) != hipSuccess) return DIT_ERR_HIP;
+      ws_bytes = dit::kScratchBytes;
+    }
     return run_partitioned(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
                            cache_valid, cache_o, cache_lse, out, lse, softmax_scale, importance_out, delta_out, ws,
                            ws_bytes, false, stream);

@@ -148,8 +148,7 @@ template <int D, bool FP8>
 __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_kernel(
     const u16 *__restrict__ q, const u16 *__restrict__ k, const u16 *__restrict__ v,
     void *__restrict__ cache_o, float *__restrict__ cache_scale, float *__restrict__ cache_lse,
-    float *__restrict__ delta_part, const AttnDesc desc, const float scale_log2, int *__restrict__ sched,
-    const int static_per) {
+    float *__restrict__ delta_part, const AttnDesc desc, const float scale_log2) {
   using G = TileGeom<D>;
   constexpr int KK = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -171,62 +170,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   const int hh = lane >> 5;
 
   // ---- work item.  Workgroups are dealt round-robin to the 8 XCDs (workgroup w to XCD
-  // w mod 8); each XCD takes a contiguous range of the items, so that consecutive items (same
-  // K/V partition) run on one XCD and share its L2.  Without `sched` the k-th workgroup of
-  // an XCD takes the k-th item of its range.  With `sched`, the XCDs, which run at different
-  // clocks, are balanced: the first static_per items of each range are still taken that way,
-  // and the rest are claimed at run time through one counter per XCD (sched[0..7], zero at
-  // launch): a workgroup past the static part claims the next item of its own range, and
-  // once that is used up, the next item of another XCD's range.  The grid then holds
-  // spare workgroups per XCD, which exit when every item has been claimed.
+  // w mod 8); remap so that each XCD takes a contiguous range of the items: consecutive items
+  // (same K/V partition) run on one XCD and share its L2.
+  const int nwg = gridDim.x;
   const int wg = blockIdx.x;
-  const int xcd = wg & 7;
-  const int n_items = desc.B * desc.H * desc.items_per_head;
-  int item;
-  {
-    const int per = n_items >> 3, rem = n_items & 7;
-    auto range_lo = [&](int x) { return x * per + min(x, rem); };
-    auto range_n = [&](int x) { return per + (x < rem ? 1 : 0); };
-    const int k = wg >> 3;
-    if (sched == nullptr) {
-      item = range_lo(xcd) + k;
-    } else if (k < min(static_per, range_n(xcd))) {
-      item = range_lo(xcd) + k;
-    } else {
-      // dynamic part of XCD x: items [lo + ns, lo + n), ns = min(static_per, n)
-      auto dyn_n = [&](int x) { return range_n(x) - min(static_per, range_n(x)); };
-      auto dyn_lo = [&](int x) { return range_lo(x) + min(static_per, range_n(x)); };
-      __shared__ int claimed;
-      if (wave == 0) {
-        int got = -1;
-        if (lane == 0) {
-          const int t = atomicAdd(&sched[xcd], 1);
-          if (t < dyn_n(xcd)) got = dyn_lo(xcd) + t;
-        }
-        got = __shfl(got, 0);
-        // Own range used up: look at every counter at once, claim from the first XCD after
-        // this one that has items left.  A failed claim leaves that counter past its range,
-        // so the loop ends after at most 8 failures.
-        while (got < 0) {
-          const bool left = lane < 8 && __hip_atomic_load(&sched[lane], __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT) < dyn_n(lane);
-          uint32_t m = (uint32_t)__ballot(left) & 0xffu;
-          if (m == 0) break;
-          m = ((m >> ((xcd + 1) & 7)) | (m << (8 - ((xcd + 1) & 7)))) & 0xffu;  // rotate: xcd + 1 first
-          const int y = (__builtin_ctz(m) + xcd + 1) & 7;
-          if (lane == 0) {
-            const int t = atomicAdd(&sched[y], 1);
-            if (t < dyn_n(y)) got = dyn_lo(y) + t;
-          }
-          got = __shfl(got, 0);
-        }
-        if (lane == 0) claimed = got;
-      }
-      __syncthreads();
-      item = claimed;
-      if (item < 0) return;  // every item has been claimed (uniform over the workgroup)
-    }
-  }
+  const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
+  const int item = xcd * per + min(xcd, rem) + (wg >> 3);
   const int per_head = desc.items_per_head;
   const int bh = item / per_head;
   int idx = item - bh * per_head;
@@ -739,6 +688,28 @@ __device__ __forceinline__ void merge_rows(const MergeGrid &g, int w, int S_q, i
 // that are not `valid` (no loads at all) get weight 0.  An extra state (extra_lse non-null,
 // its lse at index xi loaded by lane 0) takes part in the merge with its weight in
 // wts[PMAX].  Returns the merged lse (-inf when every state is empty).
+// Reduction over the TPR lanes of a row-head group (aligned runs of TPR lanes), every lane
+// ending with the result in a fixed order.  With kMergeDpp the lanes exchange values through
+// DPP moves inside rows of 16 lanes (quad swaps, then the half-row and row mirrors), else
+// through xor shuffles (LDS permute).
+template <int TPR, typename Op>
+__device__ __forceinline__ float group_reduce(float x, Op op) {
+  if constexpr (kMergeDpp && TPR <= 16) {
+    auto dpp = [](float v, auto ctrl) {
+      return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    if constexpr (TPR >= 2) x = op(x, dpp(x, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+    if constexpr (TPR >= 4) x = op(x, dpp(x, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+    if constexpr (TPR >= 8) x = op(x, dpp(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+    if constexpr (TPR >= 16) x = op(x, dpp(x, std::integral_constant<int, 0x140>{})); // row_mirror
+    return x;
+  } else {
+#pragma unroll
+    for (int off = TPR / 2; off >= 1; off >>= 1) x = op(x, __shfl_xor(x, off));
+    return x;
+  }
+}
+
 template <int TPR, int PMAX, bool SCALED>
 __device__ __forceinline__ float group_merge_weights(const float *__restrict__ cache_lse,
                                                      const float *__restrict__ cache_scale, int64_t ci,
@@ -757,13 +728,11 @@ __device__ __forceinline__ float group_merge_weights(const float *__restrict__ c
   }
   const float lx = (valid && extra_lse != nullptr && c == 0) ? extra_lse[xi] : -INFINITY;
   M = fmaxf(M, lx);
-#pragma unroll
-  for (int off = TPR / 2; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  M = group_reduce<TPR>(M, [](float a, float b) { return fmaxf(a, b); });
   float sum = (lx > -INFINITY) ? __expf(lx - M) : 0.f;
 #pragma unroll
   for (int k = 0; k < NPL; ++k) sum += (lv[k] > -INFINITY) ? __expf(lv[k] - M) : 0.f;
-#pragma unroll
-  for (int off = TPR / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  sum = group_reduce<TPR>(sum, [](float a, float b) { return a + b; });
   const float L = (M > -INFINITY) ? M + __logf(sum) : -INFINITY;
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
@@ -828,16 +797,25 @@ __global__ __launch_bounds__(256) void state_merge_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     const u16 *src = cache_o + rh * D + 8 * c;
+    // kMergeBatch planes' loads in flight together; a short last batch re-reads plane P - 1
+    // in place of the missing ones (never added)
 #pragma unroll
-    for (int p = 0; p < PMAX; ++p) {
-      if (p < P) {
-        const float wp = wts[p];
-        const u32x4 u = __builtin_nontemporal_load((const u32x4 *)(src + p * plane_o));
-        const uint32_t x[4] = {u[0], u[1], u[2], u[3]};
+    for (int p0 = 0; p0 < PMAX; p0 += kMergeBatch) {
+      if (p0 < P) {
+        u32x4 u[kMergeBatch];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc[2 * t] += wp * bf16_bits_to_f32(x[t] & 0xffffu);
-          acc[2 * t + 1] += wp * bf16_bits_to_f32(x[t] >> 16);
+        for (int j = 0; j < kMergeBatch; ++j)
+          u[j] = __builtin_nontemporal_load((const u32x4 *)(src + (int64_t)min(p0 + j, P - 1) * plane_o));
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          if (p0 + j < P) {
+            const float wp = wts[p0 + j];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              acc[2 * t] += wp * bf16_bits_to_f32(u[j][t] & 0xffffu);
+              acc[2 * t + 1] += wp * bf16_bits_to_f32(u[j][t] >> 16);
+            }
+          }
         }
       }
     }
@@ -890,33 +868,43 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
 #pragma unroll
     for (int e = 0; e < kFp8Dpt; ++e) acc[e] = 0.f;
     const uint8_t *src = cache_q8 + rh * D + kFp8Dpt * c;
+    // kMergeBatch planes' loads in flight together (as in state_merge_kernel)
 #pragma unroll
-    for (int p = 0; p < PMAX; ++p) {
-      if (p < P) {
-        const float wp = wts[p];
-        uint32_t u[NW];
-        if constexpr (NW >= 4) {
+    for (int p0 = 0; p0 < PMAX; p0 += kMergeBatch) {
+      if (p0 < P) {
+        uint32_t u[kMergeBatch][NW];
 #pragma unroll
-          for (int q = 0; q < NW / 4; ++q) {
-            const u32x4 v4 = __builtin_nontemporal_load((const u32x4 *)(src + p * plane_o) + q);
-            u[4 * q + 0] = v4[0];
-            u[4 * q + 1] = v4[1];
-            u[4 * q + 2] = v4[2];
-            u[4 * q + 3] = v4[3];
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const uint8_t *sp = src + (int64_t)min(p0 + j, P - 1) * plane_o;
+          if constexpr (NW >= 4) {
+#pragma unroll
+            for (int q = 0; q < NW / 4; ++q) {
+              const u32x4 v4 = __builtin_nontemporal_load((const u32x4 *)sp + q);
+              u[j][4 * q + 0] = v4[0];
+              u[j][4 * q + 1] = v4[1];
+              u[j][4 * q + 2] = v4[2];
+              u[j][4 * q + 3] = v4[3];
+            }
+          } else {
+            const u32x2 v2 = __builtin_nontemporal_load((const u32x2 *)sp);
+            u[j][0] = v2[0];
+            u[j][1] = v2[1];
           }
-        } else {
-          const u32x2 v2 = __builtin_nontemporal_load((const u32x2 *)(src + p * plane_o));
-          u[0] = v2[0];
-          u[1] = v2[1];
         }
 #pragma unroll
-        for (int t = 0; t < NW; ++t) {
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[t], true);
-          acc[4 * t + 0] += wp * lo[0];
-          acc[4 * t + 1] += wp * lo[1];
-          acc[4 * t + 2] += wp * hi[0];
-          acc[4 * t + 3] += wp * hi[1];
+        for (int j = 0; j < kMergeBatch; ++j) {
+          if (p0 + j < P) {
+            const float wp = wts[p0 + j];
+#pragma unroll
+            for (int t = 0; t < NW; ++t) {
+              const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[j][t], false);
+              const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[j][t], true);
+              acc[4 * t + 0] += wp * lo[0];
+              acc[4 * t + 1] += wp * lo[1];
+              acc[4 * t + 2] += wp * hi[0];
+              acc[4 * t + 3] += wp * hi[1];
+            }
+          }
         }
       }
     }
@@ -1245,57 +1233,26 @@ int64_t merge_workgroups(int D, bool fp8_cache, const BlockDesc *imp_blocks, int
   return nwg;
 }
 
-namespace {
-// Zero `n` ints (the schedule counters of an attention launch; a kernel rather than a memset
-// so that the sequence can be captured in a graph).
-__global__ __launch_bounds__(64) void clear_ints_kernel(int *__restrict__ p, int n) {
-  // agent-scope stores: the counters are then read and updated by every XCD
-  if ((int)threadIdx.x < n) __hip_atomic_store(&p[threadIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-}  // namespace
-
-AttnLaunch attention_launch_shape(const AttnDesc &desc, bool balanced) {
-  AttnLaunch L;
-  L.n_items = (int64_t)desc.B * desc.H * desc.items_per_head;
-  L.balanced = balanced && L.n_items >= kBalanceMinItems;
-  if (!L.balanced) {
-    L.static_per = 0;
-    L.workgroups = L.n_items;
-    return L;
-  }
-  const int64_t per_max = (L.n_items + 7) / 8;
-  L.static_per = (int32_t)(per_max * kBalanceStaticPercent / 100);
-  L.workgroups = 8 * (per_max + (per_max * kBalanceSparePercent + 99) / 100 + 1);
-  return L;
-}
-
 hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, const void *k, const void *v,
                                       void *cache_o, float *cache_scale, float *cache_lse, float *delta_partials,
-                                      int *sched, const AttnDesc &desc, float scale_log2, hipStream_t stream) {
-  const AttnLaunch L = attention_launch_shape(desc, sched != nullptr);
-  if (L.n_items == 0) return hipSuccess;
+                                      const AttnDesc &desc, float scale_log2, hipStream_t stream) {
+  const int64_t nwg = (int64_t)desc.B * desc.H * desc.items_per_head;
+  if (nwg == 0) return hipSuccess;
   (void)hipGetLastError();
-  int *sc = L.balanced ? sched : nullptr;
-  if (sc != nullptr) {
-    hipLaunchKernelGGL(clear_ints_kernel, dim3(1), dim3(64), 0, stream, sc, kSchedInts);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  dim3 grid((unsigned)L.workgroups), block(kWaves * 64);
+  dim3 grid((unsigned)nwg), block(kWaves * 64);
   const u16 *qq = (const u16 *)q, *kk = (const u16 *)k, *vv = (const u16 *)v;
-  const int sp = L.static_per;
   if (D == 128 && !fp8_cache)
     hipLaunchKernelGGL((partition_attention_kernel<128, false>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
-                       cache_lse, delta_partials, desc, scale_log2, sc, sp);
+                       cache_lse, delta_partials, desc, scale_log2);
   else if (D == 128)
     hipLaunchKernelGGL((partition_attention_kernel<128, true>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
-                       cache_lse, delta_partials, desc, scale_log2, sc, sp);
+                       cache_lse, delta_partials, desc, scale_log2);
   else if (!fp8_cache)
     hipLaunchKernelGGL((partition_attention_kernel<64, false>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
-                       cache_lse, delta_partials, desc, scale_log2, sc, sp);
+                       cache_lse, delta_partials, desc, scale_log2);
   else
     hipLaunchKernelGGL((partition_attention_kernel<64, true>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
-                       cache_lse, delta_partials, desc, scale_log2, sc, sp);
+                       cache_lse, delta_partials, desc, scale_log2);
   return hipGetLastError();
 }
 

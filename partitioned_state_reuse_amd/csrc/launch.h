@@ -48,6 +48,16 @@ constexpr int kMaskedMergeBatch = DIT_MERGE_MASKED_BATCH;
 #ifndef DIT_MERGE_FP8_DPT
 #define DIT_MERGE_FP8_DPT 16
 #endif
+#ifndef DIT_MERGE_BATCH
+#define DIT_MERGE_BATCH 1
+#endif
+// cache planes whose loads a merge thread (plain and fp8 merge) keeps in flight together
+constexpr int kMergeBatch = DIT_MERGE_BATCH;
+#ifndef DIT_MERGE_DPP
+#define DIT_MERGE_DPP 0
+#endif
+// merge-weight reductions over a row-head's lanes through DPP moves instead of LDS permutes
+constexpr bool kMergeDpp = DIT_MERGE_DPP != 0;
 constexpr int kMinBlocks = DIT_ATTN_MIN_BLOCKS;     // attention workgroups resident per CU (register budget)
 
 // Work description of one partition-attention launch, passed by value as a kernel
@@ -75,37 +85,11 @@ struct BlockDesc {
   int32_t tile_prefix[DIT_MAX_BLOCKS + 1];
 };
 
-// Work balancing of the attention launch across the 8 XCDs (which run at different clocks):
-// the first kBalanceStaticPercent % of each XCD's items are placed statically, the rest are
-// claimed at run time through kSchedInts counters in the workspace; the grid holds
-// kBalanceSparePercent % spare workgroups per XCD for the claims.  Launches of fewer than
-// kBalanceMinItems items (about two rounds of the chip) stay static.
-#ifndef DIT_BALANCE_STATIC_PERCENT
-#define DIT_BALANCE_STATIC_PERCENT 80
-#endif
-#ifndef DIT_BALANCE_SPARE_PERCENT
-#define DIT_BALANCE_SPARE_PERCENT 12
-#endif
-constexpr int kBalanceStaticPercent = DIT_BALANCE_STATIC_PERCENT;
-constexpr int kBalanceSparePercent = DIT_BALANCE_SPARE_PERCENT;
-constexpr int64_t kBalanceMinItems = 1536;
-constexpr int kSchedInts = 8;
-constexpr size_t kSchedBytes = 256;  // workspace bytes reserved for the counters
-
-struct AttnLaunch {
-  int64_t n_items;      // (batch, head, partition, block, tile) items
-  int64_t workgroups;   // grid size
-  int32_t static_per;   // statically placed items per XCD
-  bool balanced;
-};
-AttnLaunch attention_launch_shape(const AttnDesc &desc, bool balanced);
-
 // fp8_cache: cache_o holds e4m3 codes (1 byte per element) and cache_scale one scale per
 // (partition, batch, head, row); otherwise cache_o is bf16 and cache_scale is unused.
-// sched: kSchedInts ints of device memory for the balanced schedule, or NULL (static).
 hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, const void *k, const void *v,
                                       void *cache_o, float *cache_scale, float *cache_lse, float *delta_partials,
-                                      int *sched, const AttnDesc &desc, float scale_log2, hipStream_t stream);
+                                      const AttnDesc &desc, float scale_log2, hipStream_t stream);
 
 // Merges.  The cache's lse (and scale) planes are [P, B, S_q, H]; the merged lse goes out as
 // [B, H, S_q], or, with lse_rowmajor, as [B, S_q, H] (a cache plane: compose).  With

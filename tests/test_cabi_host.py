@@ -45,11 +45,11 @@ def test_status_strings(L):
 
 
 def test_workspace_bytes(L):
-    # 256 bytes of schedule counters, the local-change partials: (591 + 16) 128-row query
-    # tiles x 40 heads x 2 floats, then from the next 256-byte boundary the merge's importance
-    # partials: (75,600 x 40 / 16 + 16) merge workgroups x 16 planes x 4 bytes
+    # local-change partials: (591 + 16) 128-row query tiles x 40 heads x 2 floats, then from the
+    # next 256-byte boundary the merge's importance partials: (75,600 x 40 / 16 + 16) merge
+    # workgroups x 16 planes x 4 bytes
     delta = (591 + 16) * 40 * 8
-    assert L.dit_attn_workspace_bytes(1, 75600, 40, 128, 16, 16) == (256 + delta + 255) // 256 * 256 + (189000 + 16) * 16 * 4
+    assert L.dit_attn_workspace_bytes(1, 75600, 40, 128, 16, 16) == (delta + 255) // 256 * 256 + (189000 + 16) * 16 * 4
     assert L.dit_attn_workspace_bytes(1, 100, 4, 96, 1, 1) == 0      # unsupported D
     assert L.dit_attn_workspace_bytes(1, 100, 4, 64, 0, 1) == 0      # no blocks
     assert L.dit_attn_workspace_bytes(1, 100, 4, 64, 1, 65) == 0     # too many partitions

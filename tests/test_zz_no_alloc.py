@@ -90,8 +90,8 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
     H, D = 40, 128
 
     def scratch_need(S_q, n_qb=1):
-        # schedule counters (256 B), then one (num, den) pair per (128-row query tile, head)
-        return 256 + ((S_q + 127) // 128 + n_qb) * H * 8
+        # one (num, den) pair per (128-row query tile, head)
+        return ((S_q + 127) // 128 + n_qb) * H * 8
 
     S_q = 600_000                                     # (4688 tiles + 1) * 40 * 8 B > 1 MiB
     assert scratch_need(S_q) > (1 << 20)
