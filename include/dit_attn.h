@@ -193,6 +193,42 @@ int dit_partition_attention(const void *q, const void *k, const void *v,
                             void *stream);
 
 /*
+ * Partition attention with the reuse work in the same launch: the one-GPU form of filling
+ * compute bubbles with reuse operations (DiTango, technical summary, "Methodology §2,
+ * Pipeline Orchestration").  Does what dit_partition_attention does, and in addition merges,
+ * for every query row r of block i and head h, the cache planes that block i reuses
+ * (recompute[i * P + p] = 0) into the partial state
+ *   pre_o    device out [B, S_q, H, D] bf16
+ *   pre_lse  device out [B, H, S_q] f32
+ * by the rule of dit_state_merge (a row whose block reuses no plane gets O = 0,
+ * lse = -inf).  The merging workgroups are dispatched after every attention workgroup and
+ * run in the slots that the attention work leaves as the launch drains; the planes they
+ * read are ones this launch does not write.  Finish the step with dit_state_merge_masked
+ * (plane_select = recompute, extra state = pre_o / pre_lse): a two-state final combine.
+ *   local_part   host [n_qb] or NULL: when given, the local-change partials are written
+ *                as by dit_partition_attention with a workspace (finish them with
+ *                dit_local_change_finalize); when NULL they are not.
+ *   workspace    device, required, of workspace_bytes >= dit_attn_workspace_bytes(...):
+ *                the local-change partials and a chunk counter that the call clears on its
+ *                stream before the launch.  Calls that share a workspace must not run at the
+ *                same time.
+ * pre_o / pre_lse must not overlap the cache, q, k or v.  Errors as for
+ * dit_partition_attention (bf16 cache only; DIT_ERR_WORKSPACE without a workspace).
+ */
+int dit_partition_attention_premerge(const void *q, const void *k, const void *v,
+                                     int B, int S_q, int S_kv, int H, int D,
+                                     const int32_t *q_offsets, int n_qb,
+                                     const int32_t *kv_offsets, int P,
+                                     const int32_t *local_part,
+                                     const uint8_t *recompute,
+                                     const uint8_t *cache_valid,
+                                     void *cache_o, float *cache_lse,
+                                     float softmax_scale,
+                                     void *pre_o, float *pre_lse,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/*
  * State merge: for every query row and head, compose the P cached states (all P slots,
  * as the partition-attention call left them) into out / lse by LSE-weighted combination in
  * fp32; states with lse = -inf carry no weight; if every state is empty, out = 0 and

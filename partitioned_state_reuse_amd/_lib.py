@@ -33,6 +33,10 @@ SIGNATURES = {
     "dit_partition_attention": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                         P_i32, c_int, P_i32, c_int, P_i32, P_u8, P_u8,
                                         c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p]),
+    "dit_partition_attention_premerge": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                                 P_i32, c_int, P_i32, c_int, P_i32, P_u8, P_u8,
+                                                 c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                                 c_void_p, c_size_t, c_void_p]),
     "dit_partition_attention_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                             P_i32, c_int, P_i32, c_int, P_i32, P_u8, P_u8,
                                             c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p]),

@@ -149,6 +149,24 @@ def partition_attention(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cach
         float(scale), wp, ws_bytes, _stream(stream)))
 
 
+def partition_attention_premerge(q, k, v, q_offsets, kv_offsets, recompute, cache_o, cache_lse, pre_o, pre_lse, *,
+                                 workspace, local_part=None, cache_valid=None, scale: float = 0.0,
+                                 stream=None) -> None:
+    """dit_partition_attention_premerge: partition_attention plus, in the same launch, the
+    merge of each block's reused planes into pre_o / pre_lse.  With local_part it also
+    writes the local-change partials into the workspace."""
+    (B, S_q, S_kv, H, D), (qp, kp, vp) = _qkv(q, k, v)
+    n_qb, P = len(q_offsets) - 1, len(kv_offsets) - 1
+    wp, ws_bytes = _ws(workspace, "workspace")
+    _check(_lib.lib().dit_partition_attention_premerge(
+        qp, kp, vp, B, S_q, S_kv, H, D, _i32(q_offsets), n_qb, _i32(kv_offsets), P,
+        None if local_part is None else _i32(local_part), _u8(recompute),
+        None if cache_valid is None else _u8(cache_valid),
+        _dev(cache_o, BF16, (P, B, S_q, H, D), "cache_o"), _dev(cache_lse, F32, (P, B, S_q, H), "cache_lse"),
+        float(scale), _dev(pre_o, BF16, (B, S_q, H, D), "pre_o"), _dev(pre_lse, F32, (B, H, S_q), "pre_lse"),
+        wp, ws_bytes, _stream(stream)))
+
+
 def partition_attention_fp8(q, k, v, q_offsets, kv_offsets, recompute, cache_q8, cache_scale, cache_lse, *,
                             local_part=None, cache_valid=None, scale: float = 0.0, workspace=None,
                             stream=None) -> None:
@@ -345,6 +363,29 @@ class SelectiveAttention:
         if do_delta:
             local_change_finalize(self.workspace, self.B, self.S_q, self.H, self.D, self.q_offsets, self.delta,
                                   stream=main)
+        self.valid |= recompute
+        return do_delta
+
+    def step_premerged(self, q, k, v, recompute, *, want_delta=False, scale=0.0, stream=None):
+        """One selective step with the reuse work inside the attention launch: the launch's
+        last workgroups pre-merge the reused states into a partial state in the slots that
+        the attention work leaves as it drains, then the fresh states and the partial are
+        merged (a two-state final combine per row-head, plus the fresh planes)."""
+        self._bf16_only("step_premerged")
+        recompute = np.asarray(recompute, dtype=np.uint8).reshape(self.n_qb, self.P)
+        if not hasattr(self, "partial_o"):
+            self.partial_o = torch.empty_like(self.out)
+            self.partial_lse = torch.empty_like(self.lse)
+        do_delta = want_delta and all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
+        partition_attention_premerge(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o,
+                                     self.cache_lse, self.partial_o, self.partial_lse, workspace=self.workspace,
+                                     local_part=self.local_part if do_delta else None, cache_valid=self.valid,
+                                     scale=scale, stream=stream)
+        state_merge_masked(self.cache_o, self.cache_lse, self.q_offsets, recompute, self.out, self.lse,
+                           extra_o=self.partial_o, extra_lse=self.partial_lse, stream=stream)
+        if do_delta:
+            local_change_finalize(self.workspace, self.B, self.S_q, self.H, self.D, self.q_offsets, self.delta,
+                                  stream=stream)
         self.valid |= recompute
         return do_delta
 

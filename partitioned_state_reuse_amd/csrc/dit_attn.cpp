@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <exception>
 
 #include "launch.h"
@@ -248,6 +249,59 @@ int dit_partition_attention(const void *q, const void *k, const void *v, int B, 
     if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse,
                                         want_delta ? (float *)workspace : nullptr, desc,
                                         scale_log2_of(softmax_scale, D), as_stream(stream)) != hipSuccess)
+      return DIT_ERR_HIP;
+    return DIT_OK;
+  } catch (...) {
+    return DIT_ERR_INTERNAL;
+  }
+}
+
+int dit_partition_attention_premerge(const void *q, const void *k, const void *v, int B, int S_q, int S_kv, int H,
+                                     int D, const int32_t *q_offsets, int n_qb, const int32_t *kv_offsets, int P,
+                                     const int32_t *local_part, const uint8_t *recompute, const uint8_t *cache_valid,
+                                     void *cache_o, float *cache_lse, float softmax_scale, void *pre_o,
+                                     float *pre_lse, void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    if (!pre_o || !pre_lse) return DIT_ERR_NULL;
+    AttnDesc desc;
+    const bool want_delta = local_part != nullptr;
+    int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
+                        cache_valid, cache_o, cache_lse, want_delta, workspace, workspace_bytes, desc);
+    if (st) return st;
+    // the claim counter sits at the start of the workspace's second region
+    if (!workspace) return DIT_ERR_WORKSPACE;
+    const size_t claim_off = imp_ws_offset(B, S_q, H, n_qb);
+    if (workspace_bytes < claim_off + sizeof(uint32_t)) return DIT_ERR_WORKSPACE;
+    dit::TailMerge tm;
+    memset(&tm, 0, sizeof(tm));
+    tm.pre_o = pre_o;
+    tm.pre_lse = pre_lse;
+    tm.claim = (uint32_t *)((char *)workspace + claim_off);
+    for (int i = 0; i < n_qb; ++i)
+      for (int p = 0; p < P; ++p)
+        if (!recompute[i * P + p]) tm.reuse_mask[i] |= (uint64_t)1 << p;
+    // chunks: about 8 per resident workgroup slot of the device, 1 to 16 passes each
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return DIT_ERR_HIP;
+    const int64_t slots = std::max<int64_t>(1, (int64_t)cus * dit::kMinBlocks);
+    const int64_t rpw = 256 / (D / 8);
+    const int64_t passes = ((int64_t)B * S_q * H + rpw - 1) / rpw;
+    const int64_t chunk_passes = std::min<int64_t>(16, std::max<int64_t>(1, passes / (8 * slots)));
+    const int64_t n_chunks = (passes + chunk_passes - 1) / chunk_passes;
+    const int64_t n_attn = (int64_t)B * H * desc.items_per_head;
+    const int64_t n_tail = std::min(n_chunks, slots);
+    // every tail workgroup ends with one failed claim: the counter reaches n_chunks + n_tail
+    if ((n_attn + n_tail) * (dit::kWaves * 64) > (int64_t)UINT32_MAX || n_chunks + n_tail > (int64_t)UINT32_MAX)
+      return DIT_ERR_SHAPE;
+    tm.n_attn_wg = (int32_t)n_attn;
+    tm.n_tail_wg = (int32_t)n_tail;
+    tm.n_chunks = (int32_t)n_chunks;
+    tm.chunk_passes = (int32_t)chunk_passes;
+    if (dit::launch_partition_attention_premerge(D, q, k, v, cache_o, cache_lse,
+                                                 want_delta ? (float *)workspace : nullptr, desc,
+                                                 scale_log2_of(softmax_scale, D), tm, as_stream(stream)) != hipSuccess)
       return DIT_ERR_HIP;
     return DIT_OK;
   } catch (...) {

@@ -144,11 +144,13 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The work of one attention workgroup: workgroup `wg` of the `nwg` that carry attention
+// items.
 template <int D, bool FP8>
-__global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_kernel(
+__device__ __forceinline__ void attention_item(
     const u16 *__restrict__ q, const u16 *__restrict__ k, const u16 *__restrict__ v,
     void *__restrict__ cache_o, float *__restrict__ cache_scale, float *__restrict__ cache_lse,
-    float *__restrict__ delta_part, const AttnDesc desc, const float scale_log2) {
+    float *__restrict__ delta_part, const AttnDesc &desc, const float scale_log2, const int nwg, const int wg) {
   using G = TileGeom<D>;
   constexpr int KK = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -172,8 +174,6 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   // ---- work item.  Workgroups are dealt round-robin to the 8 XCDs (workgroup w to XCD
   // w mod 8); remap so that each XCD takes a contiguous range of the items: consecutive items
   // (same K/V partition) run on one XCD and share its L2.
-  const int nwg = gridDim.x;
-  const int wg = blockIdx.x;
   const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
   const int item = xcd * per + min(xcd, rem) + (wg >> 3);
   const int per_head = desc.items_per_head;
@@ -488,6 +488,24 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
   // per row), so that the column-wise writes and the row-wise reads are free of bank
   // conflicts.
   static_assert(kWaves <= 4, "one staging buffer per wave");
+  // Cache slots are written once per step and read back only by the merge (and, for a local
+  // partition, the old slot once by this epilogue): with kNtSlots they are streamed with
+  // non-temporal accesses, so that they do not displace the K/V tiles other workgroups still
+  // read from L2.
+  auto store_slot = [](uint4 *dst, const uint4 &v) {
+    if constexpr (kNtSlots)
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4 *)dst);
+    else
+      *dst = v;
+  };
+  auto load_slot = [](const uint4 *src) -> uint4 {
+    if constexpr (kNtSlots) {
+      const u32x4 u = __builtin_nontemporal_load((const u32x4 *)src);
+      return make_uint4(u[0], u[1], u[2], u[3]);
+    } else {
+      return *src;
+    }
+  };
   char *stg = (char *)(wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1);
   auto slot_of = [&](int r) {  // [P, B, S_q] index of query row r of this tile
     return ((int64_t)p * desc.B + b) * desc.S_q + q0 + r;
@@ -530,7 +548,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       if (wave * 32 + r < qn) {
         uint8_t *dst = (uint8_t *)cache_o + (slot_of(wave * 32 + r) * H + head) * D + col * 16;
         if (is_local) {
-          const uint4 od = *(const uint4 *)dst;
+          const uint4 od = load_slot((const uint4 *)dst);
           const float old_s = cache_scale[lslot_of(wave * 32 + r)];
           const float new_s = stg_scale[r];
           const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w}, oo[4] = {od.x, od.y, od.z, od.w};
@@ -549,7 +567,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
             }
           }
         }
-        *(uint4 *)dst = nw;
+        store_slot((uint4 *)dst, nw);
       }
     }
     // after the old scales have been read above
@@ -578,7 +596,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       if (wave * 32 + r < qn) {
         u16 *dst = (u16 *)cache_o + (slot_of(wave * 32 + r) * H + head) * D + col * 8;
         if (is_local) {
-          const uint4 od = *(const uint4 *)dst;
+          const uint4 od = load_slot((const uint4 *)dst);
           const uint32_t nn[4] = {nw.x, nw.y, nw.z, nw.w}, oo[4] = {od.x, od.y, od.z, od.w};
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -588,7 +606,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
             dden += o0 * o0 + o1 * o1;
           }
         }
-        *(uint4 *)dst = nw;
+        store_slot((uint4 *)dst, nw);
       }
     }
     if (qvalid && hh == 0) cache_lse[lslot_of(qrow)] = lse_nat;
@@ -617,6 +635,15 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_k
       dp[1] = d;
     }
   }
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_kernel(
+    const u16 *__restrict__ q, const u16 *__restrict__ k, const u16 *__restrict__ v,
+    void *__restrict__ cache_o, float *__restrict__ cache_scale, float *__restrict__ cache_lse,
+    float *__restrict__ delta_part, const AttnDesc desc, const float scale_log2) {
+  attention_item<D, FP8>(q, k, v, cache_o, cache_scale, cache_lse, delta_part, desc, scale_log2, gridDim.x,
+                         blockIdx.x);
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs (workgroup w runs on XCD w mod 8), and
@@ -924,40 +951,23 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
   if constexpr (IMP) importance_partials<RPW, PMAX>(wraw_all, P, w, imp_part);
 }
 
-// Masked merge: as state_merge_kernel, but row r of query block i combines only the planes
-// selected for block i, plus an optional extra state (a partial composition made earlier,
-// its lse in the [B, H, S_q] layout of a merged output).
-// Used to pre-merge the reused states on a second stream while the attention kernel
-// recomputes the others, and to finish with the fresh states and that partial.
+// Masked merge of one row-head rh by its TPR lanes (this lane is number c of them): the
+// cache planes in pm, in increasing order, plus the extra state when extra_lse is non-null
+// (a partial composition made earlier, its lse in the [B, H, S_q] layout of a merged output,
+// at index xi, which is also where the merged lse goes).  wts: the group's PMAX + 1 weights
+// in LDS.
 template <int D, int PMAX>
-__global__ __launch_bounds__(256) void state_merge_masked_kernel(
-    const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, const u16 *__restrict__ extra_o,
-    const float *__restrict__ extra_lse, const MergeSelect sel, u16 *__restrict__ out,
-    float *__restrict__ lse_out, const int S_q, const int H, const int P, const int64_t total_rh,
-    const int64_t plane_o, const int64_t plane_lse, const int chunk) {
+__device__ __forceinline__ void masked_merge_rowhead(const u16 *__restrict__ cache_o,
+                                                     const float *__restrict__ cache_lse,
+                                                     const u16 *__restrict__ extra_o,
+                                                     const float *__restrict__ extra_lse, u16 *__restrict__ out,
+                                                     float *__restrict__ lse_out, const int64_t rh,
+                                                     const int64_t xi, const uint64_t pm, const int P,
+                                                     const int64_t plane_o, const int64_t plane_lse, const int c,
+                                                     float *wts) {
   constexpr int TPR = D / 8;
-  constexpr int RPW = 256 / TPR;
-  const int64_t rh = (int64_t)lse_chunked_item(chunk) * RPW + threadIdx.x / TPR;
-  if (rh >= total_rh) return;
-  const int c = threadIdx.x % TPR;
-  const int64_t br = rh / H;
-  const int h = (int)(rh - br * H);
-  const int64_t b = br / S_q;
-  const int r = (int)(br - b * S_q);
-  const int64_t lo_idx = (b * H + h) * S_q + r;
-  // block of row r: last i with q_off[i] <= r
-  int lo = 0, hi = sel.n_qb - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (sel.q_off[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  const uint64_t pm = sel.plane_mask[lo];
-
-  __shared__ float wts_all[RPW][PMAX + 1];
-  float *wts = wts_all[threadIdx.x / TPR];
   const float L = group_merge_weights<TPR, PMAX, false>(cache_lse, nullptr, rh, plane_lse, P, c, true, wts, nullptr,
-                                                        pm, sel.has_extra ? extra_lse : nullptr, lo_idx);
-
+                                                        pm, extra_lse, xi);
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -1003,14 +1013,114 @@ __global__ __launch_bounds__(256) void state_merge_masked_kernel(
       }
     }
   }
-  if (sel.has_extra) add(extra_o + rh * D + 8 * c, wts[PMAX]);
+  if (extra_lse != nullptr) add(extra_o + rh * D + 8 * c, wts[PMAX]);
   uint4 res;
   res.x = pack_bf16x2(acc[0], acc[1]);
   res.y = pack_bf16x2(acc[2], acc[3]);
   res.z = pack_bf16x2(acc[4], acc[5]);
   res.w = pack_bf16x2(acc[6], acc[7]);
   __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
-  if (c == 0) lse_out[lo_idx] = L;
+  if (c == 0) lse_out[xi] = L;
+}
+
+// Block of query row r: the last i with q_off[i] <= r.
+__device__ __forceinline__ int block_of_row(const int32_t *q_off, int n_qb, int r) {
+  int lo = 0, hi = n_qb - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (q_off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Masked merge: as state_merge_kernel, but row r of query block i combines only the planes
+// selected for block i, plus an optional extra state (a partial composition made earlier,
+// its lse in the [B, H, S_q] layout of a merged output).
+// Used to pre-merge the reused states on a second stream while the attention kernel
+// recomputes the others, and to finish with the fresh states and that partial.
+template <int D, int PMAX>
+__global__ __launch_bounds__(256) void state_merge_masked_kernel(
+    const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, const u16 *__restrict__ extra_o,
+    const float *__restrict__ extra_lse, const MergeSelect sel, u16 *__restrict__ out,
+    float *__restrict__ lse_out, const int S_q, const int H, const int P, const int64_t total_rh,
+    const int64_t plane_o, const int64_t plane_lse, const int chunk) {
+  constexpr int TPR = D / 8;
+  constexpr int RPW = 256 / TPR;
+  const int64_t rh = (int64_t)lse_chunked_item(chunk) * RPW + threadIdx.x / TPR;
+  if (rh >= total_rh) return;
+  const int c = threadIdx.x % TPR;
+  const int64_t br = rh / H;
+  const int h = (int)(rh - br * H);
+  const int64_t b = br / S_q;
+  const int r = (int)(br - b * S_q);
+  const uint64_t pm = sel.plane_mask[block_of_row(sel.q_off, sel.n_qb, r)];
+  __shared__ float wts_all[RPW][PMAX + 1];
+  masked_merge_rowhead<D, PMAX>(cache_o, cache_lse, extra_o, sel.has_extra ? extra_lse : nullptr, out, lse_out, rh,
+                                (b * H + h) * S_q + r, pm, P, plane_o, plane_lse, c, wts_all[threadIdx.x / TPR]);
+}
+
+// ------------------------------------------------------------------------------------
+// Partition attention with the reuse work in its tail.  The launch carries the attention
+// items' workgroups first and then tm.n_tail_wg more; the dispatcher hands workgroups out in
+// order, so the extra ones start only once every attention item has started, in the slots
+// that attention workgroups leave as the launch drains (the XCDs do not finish together).
+// Each extra workgroup claims chunks of row-heads from the counter tm.claim (zero at the
+// launch) until none is left, and merges, for every row-head of a chunk, the cache planes
+// its query block reuses (tm.reuse_mask) into the partial state pre_o / pre_lse: the
+// masked merge, on planes that this launch does not write.  Chunks are claimed in order, so
+// the XCDs that run out of attention items first take more of them.
+// ------------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void premerge_chunks(const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse,
+                                                const AttnDesc &desc, const TailMerge &tm) {
+  constexpr int TPR = D / 8;
+  constexpr int RPW = 256 / TPR;  // row-heads per pass of the workgroup
+  constexpr int PMAX = DIT_MAX_PARTITIONS;
+  static_assert(kWaves * 64 == 256, "the pre-merge takes 256 threads per workgroup");
+  __shared__ float wts_all[RPW][PMAX + 1];
+  __shared__ uint32_t claimed;
+  const int S_q = desc.S_q, H = desc.H;
+  const int64_t total_rh = (int64_t)desc.B * S_q * H;
+  const int64_t plane_o = total_rh * D;
+  const int c = threadIdx.x % TPR;
+  float *wts = wts_all[threadIdx.x / TPR];
+  u16 *pre_o = (u16 *)tm.pre_o;
+  for (;;) {
+    if (threadIdx.x == 0) claimed = __hip_atomic_fetch_add(tm.claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t ch = claimed;
+    __syncthreads();  // every thread has read it before the next claim overwrites it
+    if (ch >= (uint32_t)tm.n_chunks) return;
+    const int64_t rh_first = (int64_t)ch * tm.chunk_passes * RPW + threadIdx.x / TPR;
+    for (int j = 0; j < tm.chunk_passes; ++j) {
+      const int64_t rh = rh_first + (int64_t)j * RPW;
+      if (rh >= total_rh) break;
+      const int64_t br = rh / H;
+      const int h = (int)(rh - br * H);
+      const int64_t b = br / S_q;
+      const int r = (int)(br - b * S_q);
+      const uint64_t pm = tm.reuse_mask[block_of_row(desc.q_off, desc.n_qb, r)];
+      masked_merge_rowhead<D, PMAX>(cache_o, cache_lse, nullptr, nullptr, pre_o, tm.pre_lse, rh,
+                                    (b * H + h) * S_q + r, pm, desc.P, plane_o, total_rh, c, wts);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_premerge_kernel(
+    const u16 *__restrict__ q, const u16 *__restrict__ k, const u16 *__restrict__ v, void *__restrict__ cache_o,
+    float *__restrict__ cache_lse, float *__restrict__ delta_part, const AttnDesc desc, const float scale_log2,
+    const TailMerge tm) {
+  if ((int)blockIdx.x >= tm.n_attn_wg) {
+    premerge_chunks<D>((const u16 *)cache_o, cache_lse, desc, tm);
+    return;
+  }
+  attention_item<D, false>(q, k, v, cache_o, nullptr, cache_lse, delta_part, desc, scale_log2, tm.n_attn_wg,
+                           blockIdx.x);
+}
+
+__global__ void clear_claim_kernel(uint32_t *claim) {
+  if (threadIdx.x == 0) *claim = 0u;
 }
 
 template <int D>
@@ -1253,6 +1363,24 @@ hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, cons
   else
     hipLaunchKernelGGL((partition_attention_kernel<64, true>), grid, block, 0, stream, qq, kk, vv, cache_o, cache_scale,
                        cache_lse, delta_partials, desc, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_partition_attention_premerge(int D, const void *q, const void *k, const void *v, void *cache_o,
+                                               float *cache_lse, float *delta_partials, const AttnDesc &desc,
+                                               float scale_log2, const TailMerge &tm, hipStream_t stream) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(clear_claim_kernel, dim3(1), dim3(64), 0, stream, tm.claim);
+  const int64_t nwg = (int64_t)tm.n_attn_wg + tm.n_tail_wg;
+  if (nwg == 0) return hipGetLastError();
+  dim3 grid((unsigned)nwg), block(kWaves * 64);
+  const u16 *qq = (const u16 *)q, *kk = (const u16 *)k, *vv = (const u16 *)v;
+  if (D == 128)
+    hipLaunchKernelGGL((partition_attention_premerge_kernel<128>), grid, block, 0, stream, qq, kk, vv, cache_o,
+                       cache_lse, delta_partials, desc, scale_log2, tm);
+  else
+    hipLaunchKernelGGL((partition_attention_premerge_kernel<64>), grid, block, 0, stream, qq, kk, vv, cache_o,
+                       cache_lse, delta_partials, desc, scale_log2, tm);
   return hipGetLastError();
 }
 

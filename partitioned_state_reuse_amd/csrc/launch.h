@@ -30,6 +30,11 @@ constexpr int kStages = DIT_ATTN_STAGES;    // K/V tile buffers in the LDS ring 
 #endif
 // MFMAs by which the LDS operand reads run ahead of their use in the attention kernel
 constexpr int kReadAhead = DIT_ATTN_READ_AHEAD;
+#ifndef DIT_ATTN_NT_SLOTS
+#define DIT_ATTN_NT_SLOTS 0
+#endif
+// cache-slot stores (and old-slot loads) of the attention epilogue non-temporal
+constexpr bool kNtSlots = DIT_ATTN_NT_SLOTS != 0;
 #ifndef DIT_ATTN_SETPRIO
 #define DIT_ATTN_SETPRIO 0
 #endif
@@ -90,6 +95,27 @@ struct BlockDesc {
 hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, const void *k, const void *v,
                                       void *cache_o, float *cache_scale, float *cache_lse, float *delta_partials,
                                       const AttnDesc &desc, float scale_log2, hipStream_t stream);
+
+// Reuse work carried by a partition-attention launch (bf16 cache): n_tail_wg workgroups
+// after the n_attn_wg attention ones merge, for every query row, the cache planes its block
+// reuses (bit p of reuse_mask[i]: block i reuses plane p) into the partial state pre_o
+// [B, S_q, H, D] bf16, pre_lse [B, H, S_q] f32, claiming chunks of chunk_passes * 256 / (D / 8)
+// row-heads (n_chunks of them cover B * S_q * H) from the counter `claim`, which the launch
+// clears first.
+struct TailMerge {
+  void *pre_o;
+  float *pre_lse;
+  uint32_t *claim;
+  int32_t n_attn_wg;
+  int32_t n_tail_wg;
+  int32_t n_chunks;
+  int32_t chunk_passes;
+  uint64_t reuse_mask[DIT_MAX_BLOCKS];
+};
+
+hipError_t launch_partition_attention_premerge(int D, const void *q, const void *k, const void *v, void *cache_o,
+                                               float *cache_lse, float *delta_partials, const AttnDesc &desc,
+                                               float scale_log2, const TailMerge &tm, hipStream_t stream);
 
 // Merges.  The cache's lse (and scale) planes are [P, B, S_q, H]; the merged lse goes out as
 // [B, H, S_q], or, with lse_rowmajor, as [B, S_q, H] (a cache plane: compose).  With

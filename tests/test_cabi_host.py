@@ -180,6 +180,22 @@ def _u8(s):
     # dit_partition_attention(q, k, v, B, S_q, S_kv, H, D, qo, n_qb, ko, P, local, rec, valid, o, lse, sm, ws, wsb, st)
     (lambda L: L.dit_partition_attention(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2, _i32([0]),
                                          _u8([1, 0]), _u8([1, 0]), 1, 1, 0.0, None, 0, None), -5),
+    # dit_partition_attention_premerge(q, k, v, B, S_q, S_kv, H, D, qo, n_qb, ko, P, local, rec, valid, o, lse, sm,
+    #                                  pre_o, pre_lse, ws, wsb, st): the partial state's buffers, the workspace
+    #                                  (local-change partials and the chunk counter from the first 256-byte
+    #                                  boundary past them: 260 bytes here), the mask and the validity bitmap
+    (lambda L: L.dit_partition_attention_premerge(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2,
+                                                  None, _u8([1, 0]), None, 1, 1, 0.0, None, 1, 1, 1 << 20, None), -1),
+    (lambda L: L.dit_partition_attention_premerge(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2,
+                                                  None, _u8([1, 0]), None, 1, 1, 0.0, 1, 1, None, 0, None), -6),
+    (lambda L: L.dit_partition_attention_premerge(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2,
+                                                  _i32([0]), _u8([1, 0]), None, 1, 1, 0.0, 1, 1, 1, 256, None), -6),
+    (lambda L: L.dit_partition_attention_premerge(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2,
+                                                  None, _u8([1, 0]), _u8([1, 0]), 1, 1, 0.0, 1, 1, 1, 1 << 20, None), -5),
+    (lambda L: L.dit_partition_attention_premerge(1, 1, 1, 1, 8, 8, 1, 64, _i32([0, 8]), 1, _i32([0, 4, 8]), 2,
+                                                  _i32([0]), _u8([0, 1]), None, 1, 1, 0.0, 1, 1, 1, 1 << 20, None), -4),
+    (lambda L: L.dit_partition_attention_premerge(1, 1, 1, 1, 8, 8, 1, 96, _i32([0, 8]), 1, _i32([0, 4, 8]), 2,
+                                                  None, _u8([1, 0]), None, 1, 1, 0.0, 1, 1, 1, 1 << 20, None), -7),
     # dit_state_merge_fp8(q8, scale, lse, B, S_q, H, D, P, out, lse_out, qo, n_qb, imp, ws, wsb, st)
     (lambda L: L.dit_state_merge_fp8(1, None, 1, 1, 8, 1, 64, 2, 1, 1, None, 0, None, None, 0, None), -1),
     (lambda L: L.dit_state_merge_fp8(1, 1, 1, 1, 8, 1, 64, 65, 1, 1, None, 0, None, None, 0, None), -2),

@@ -1,0 +1,125 @@
+"""GPU parity of the step with the reuse work inside the attention launch
+(dit_partition_attention_premerge, then the masked two-state final combine): the output,
+the partial state of the reused planes and the local change against the oracle, and
+bitwise agreement with the two-stream step, whose pre-merge is the same arithmetic."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads as W
+import _parity as PT
+from partitioned_state_reuse_amd import api
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _partial_ref(o: PT.OracleRun, mask, rows, qo):
+    """The oracle's merge of each row's reused planes (its block's recompute flag 0)."""
+    blk = oracle.block_of_rows(rows, qo)
+    P = mask.shape[1]
+    sel = [(1 - mask[blk, p]).astype(bool) for p in range(P)]
+    Os = [np.where(sel[p][:, None, None], o.cache.stored_O[p], 0.0) for p in range(P)]
+    Ls = [np.where(sel[p][None, :], o.cache.stored_lse[p], -np.inf) for p in range(P)]
+    return oracle.merge_states(Os, Ls)
+
+
+def _check_premerged_step(w, mask, rows, qo=None, ko=None, local=None):
+    qo = list(qo if qo is not None else w.q_offsets)
+    g = PT.GpuRun(w, q_offsets=qo, kv_offsets=ko, local_part=local)
+    o = PT.OracleRun(w, rows, q_offsets=qo, kv_offsets=ko, local_part=local)
+    ones = np.ones_like(mask)
+    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
+    g.step(Xp, ones)
+    o.step(Xp, ones)
+    old = o.local_states()
+    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
+    did = g.sa.step_premerged(q, k, v, mask, want_delta=True)
+    torch.cuda.synchronize()
+    assert did
+    res = o.step(X, mask)
+    cmp = PT.compare_out(g.out_rows(rows), g.lse_rows(rows), res)
+    _log(w.name, "premerged step", cmp)
+    assert cmp.ok(), str(cmp)
+    # the partial state is the merge of the reused planes; rows whose block reuses nothing
+    # hold the empty state
+    rO, rL = _partial_ref(o, mask, rows, qo)
+    ridx = torch.as_tensor(rows, device="cuda")
+    pO = PT.bf16_to_f64(g.sa.partial_o[0, ridx])
+    pL = g.sa.partial_lse[0][:, ridx].double().cpu().numpy()
+    PT.assert_rows_close(pO, rO, "partial state of the reused planes")
+    fin = np.isfinite(rL)
+    assert (np.isneginf(pL) == ~fin).all()
+    assert np.abs(pL[fin] - rL[fin]).max() <= PT.LSE_ABS_TOL
+    assert (pO[~fin.T] == 0).all()
+    # the local change against the oracle's
+    d_r = oracle.local_change(o.local_states(), old, rows, qo)
+    assert np.allclose(g.sa.delta[0].cpu().numpy(), d_r, rtol=PT.DELTA_REL_TOL)
+    # the same step again through the two-stream path (the recomputed planes are rewritten
+    # with the same values): its pre-merge is the same arithmetic, so both agree bitwise
+    out1, lse1 = g.sa.out.clone(), g.sa.lse.clone()
+    p1, pl1 = g.sa.partial_o.clone(), g.sa.partial_lse.clone()
+    g.sa.step_overlapped(q, k, v, mask, side_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert torch.equal(g.sa.partial_o.view(torch.int16), p1.view(torch.int16))
+    assert torch.equal(g.sa.partial_lse, pl1)
+    assert torch.equal(g.sa.out.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(g.sa.lse, lse1)
+
+
+def test_premerged_step_video720p_reduced_grid():
+    w = W.workload("video720p", grid=(5, 18, 32), H=4)
+    mask, _, _, _ = PT.masks_from_planners(w)
+    _check_premerged_step(w, np.asarray(mask, np.uint8), np.arange(w.S_q))
+
+
+def test_premerged_step_share32_reduced_grid():
+    w = W.workload("share32", grid=(9, 18, 32), H=4)
+    mask, _, _, _ = PT.masks_from_planners(w)
+    _check_premerged_step(w, np.asarray(mask, np.uint8), np.arange(w.S_q))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_premerged_step_empty_partition_and_one_row_block(D):
+    qo = [0, 1, 130, 300]
+    ko = [0, 70, 70, 200, 333]      # partition 1 is empty
+    w = W.Workload(name=f"custom_pm{D}", H=3, D=D, grid=(333,), P=4, q_token_range=(0, 300), q_offsets=qo,
+                   local_part=[0] * 3, group_offsets=[0, 4], recompute_groups=1, mode="distance", seed=78,
+                   prev_scale=0.05)
+    mask = np.array([[1, 1, 0, 1], [0, 1, 1, 0], [1, 0, 0, 1]], np.uint8)
+    _check_premerged_step(w, mask, np.arange(300), qo=qo, ko=ko, local=[0, 2, 3])
+
+
+def test_premerged_step_with_nothing_reused():
+    """An anchor step: every plane recomputed, the partial state is empty everywhere and the
+    output equals the plain step's."""
+    w = W.workload("video720p", grid=(5, 18, 32), H=2)
+    ones = np.ones((w.n_qb, w.P), np.uint8)
+    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
+    g = PT.GpuRun(w)
+    g.step(Xp, ones)
+    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
+    g.sa.step(q, k, v, ones)
+    torch.cuda.synchronize()
+    out0, lse0 = g.sa.out.clone(), g.sa.lse.clone()
+    g.sa.step_premerged(q, k, v, ones)
+    torch.cuda.synchronize()
+    assert (g.sa.partial_o.float() == 0).all() and torch.isneginf(g.sa.partial_lse).all()
+    # the final combine takes the fresh planes in the plain merge's order (the empty partial
+    # has weight 0): equal up to the rounding of the last bf16 digit
+    assert torch.allclose(g.sa.out.float(), out0.float(), rtol=2.0 ** -7, atol=1e-6)
+    assert torch.allclose(g.sa.lse, lse0, rtol=0, atol=1e-6)
+
+
+def test_premerged_step_refuses_a_never_computed_slot():
+    w = W.workload("tiny")
+    g = PT.GpuRun(w)
+    X = W.make_step(w, 0)
+    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
+    with pytest.raises(api.DitError):
+        g.sa.step_premerged(q, k, v, np.array([[1, 1, 0, 0]], np.uint8))
