@@ -109,16 +109,18 @@ def summarize_profile(db_path: str) -> str:
         disp = con.execute("select name, start, end from kernels order by start").fetchall()
     except Exception:
         disp = []
-    attn = [(a, b) for n, a, b in disp if "partition_attention_kernel" in n]
+    attn = [(a, b) for n, a, b in disp if "partition_attention" in n]
     masked = [(a, b) for n, a, b in disp if "state_merge_masked_kernel" in n]
     if attn and masked:
         lines.append("")
-        lines.append("# masked merges (two-stream step) against the attention dispatches they overlap (us):")
+        lines.append("# masked merges (two-stream and pre-merged steps) against the attention dispatches they overlap (us):")
         lines.append(f"{'merge start':>12} {'merge dur':>10} {'overlap':>10} {'attn start':>12} {'attn dur':>10}")
         t0 = min(a for a, _ in attn + masked)
         for a, b in masked:
             best = max(attn, key=lambda ab: max(0, min(b, ab[1]) - max(a, ab[0])))
             ov = max(0, min(b, best[1]) - max(a, best[0]))
+            if ov == 0:   # no overlap: the attention dispatch this merge follows
+                best = max((ab for ab in attn if ab[1] <= a), key=lambda ab: ab[1], default=best)
             lines.append(f"{(a - t0) / 1e3:>12.1f} {(b - a) / 1e3:>10.1f} {ov / 1e3:>10.1f} {(best[0] - t0) / 1e3:>12.1f} "
                          f"{(best[1] - best[0]) / 1e3:>10.1f}")
     return "\n".join(lines)
@@ -195,7 +197,10 @@ def summarize_pmc(workload: str, out_json: str, fetch_dir: str, write_dir: str, 
     for (name, grid), rec in fetch.items():
         if "copyBuffer" in name or (name, grid) not in write:
             continue
-        if not ((name.startswith("dit::partition_attention") and grid == attn_grid) or
+        # the attention launch, the one with the reuse pre-merge in its tail (at most 4,096
+        # more workgroups), the merges and reductions
+        if not ((name.startswith("dit::partition_attention_kernel") and grid == attn_grid) or
+                (name.startswith("dit::partition_attention_premerge") and attn_grid < grid <= attn_grid + (1 << 20)) or
                 (not name.startswith("dit::partition_attention") and grid in grids)):
             continue
         fk, wk = pmc_mean(rec, "FETCH_SIZE"), pmc_mean(write[(name, grid)], "WRITE_SIZE")
