@@ -123,3 +123,27 @@ def test_premerged_step_refuses_a_never_computed_slot():
     q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
     with pytest.raises(api.DitError):
         g.sa.step_premerged(q, k, v, np.array([[1, 1, 0, 0]], np.uint8))
+
+
+def test_premerged_batch_of_two_matches_single_batches():
+    """B = 2: each batch's output, partial state and local change equal those of the same
+    batch run alone (the row-heads of both batches share the chunks of one launch)."""
+    H, D, S = 2, 128, 400
+    qo, ko = [0, 150, 400], [0, 100, 250, 400]
+    torch.manual_seed(1)
+    qp, kp, vp = (torch.randn(2, S, H, D, device="cuda").to(torch.bfloat16) for _ in range(3))
+    q, k, v = (t + 0.05 * torch.randn_like(t.float()).to(torch.bfloat16) for t in (qp, kp, vp))
+    ones = np.ones((2, 3), np.uint8)
+    mask = np.array([[1, 0, 1], [0, 1, 1]], np.uint8)
+    sa2 = api.SelectiveAttention(2, S, S, H, D, qo, ko, [0, 1])
+    sa2.step(qp, kp, vp, ones)
+    assert sa2.step_premerged(q, k, v, mask, want_delta=True)
+    for b in range(2):
+        one = lambda t: t[b:b + 1].contiguous()
+        sa1 = api.SelectiveAttention(1, S, S, H, D, qo, ko, [0, 1])
+        sa1.step(one(qp), one(kp), one(vp), ones)
+        assert sa1.step_premerged(one(q), one(k), one(v), mask, want_delta=True)
+        torch.cuda.synchronize()
+        assert torch.equal(sa1.partial_o[0], sa2.partial_o[b]) and torch.equal(sa1.partial_lse[0], sa2.partial_lse[b])
+        assert torch.equal(sa1.out[0], sa2.out[b]) and torch.equal(sa1.lse[0], sa2.lse[b])
+        assert torch.equal(sa1.delta[0], sa2.delta[b])
