@@ -147,3 +147,44 @@ def test_premerged_batch_of_two_matches_single_batches():
         assert torch.equal(sa1.partial_o[0], sa2.partial_o[b]) and torch.equal(sa1.partial_lse[0], sa2.partial_lse[b])
         assert torch.equal(sa1.out[0], sa2.out[b]) and torch.equal(sa1.lse[0], sa2.lse[b])
         assert torch.equal(sa1.delta[0], sa2.delta[b])
+
+
+def _check_premerged_sampled(w, rows):
+    """Full-size layout in the benchmark's launch configuration, checked on sampled rows:
+    output and partial state against the oracle, and bitwise against the two-stream step."""
+    mask = np.asarray(PT.masks_from_planners(w)[0], np.uint8)
+    ones = np.ones((w.n_qb, w.P), np.uint8)
+    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
+    g = PT.GpuRun(w)
+    g.step(Xp, ones)
+    o = PT.OracleRun(w, rows)
+    o.step(Xp, ones)
+    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
+    g.sa.step_premerged(q, k, v, mask, want_delta=True)
+    torch.cuda.synchronize()
+    res = o.step(X, mask)
+    cmp = PT.compare_out(g.out_rows(rows), g.lse_rows(rows), res)
+    _log(w.name, "premerged step, sampled rows", cmp)
+    assert cmp.ok(), str(cmp)
+    rO, rL = _partial_ref(o, mask, rows, w.q_offsets)
+    ridx = torch.as_tensor(rows, device="cuda")
+    PT.assert_rows_close(PT.bf16_to_f64(g.sa.partial_o[0, ridx]), rO, "partial state of the reused planes")
+    pL = g.sa.partial_lse[0][:, ridx].double().cpu().numpy()
+    fin = np.isfinite(rL)
+    assert (np.isneginf(pL) == ~fin).all() and np.abs(pL[fin] - rL[fin]).max() <= PT.LSE_ABS_TOL
+    out1, p1 = g.sa.out.clone(), g.sa.partial_o.clone()
+    g.sa.step_overlapped(q, k, v, mask, side_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert torch.equal(g.sa.partial_o.view(torch.int16), p1.view(torch.int16))
+    assert torch.equal(g.sa.out.view(torch.int16), out1.view(torch.int16))
+
+
+def test_premerged_step_share32_full_size_sampled_rows():
+    w = W.workload("share32")
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(1000, 1016), np.arange(2330, 2363)]))
+    _check_premerged_sampled(w, rows)
+
+
+def test_premerged_step_video720p_full_size_sampled_rows():
+    w = W.workload("video720p")
+    _check_premerged_sampled(w, W.sample_rows(w, tiles_per_block=2, tile=16))
