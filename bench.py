@@ -725,9 +725,102 @@ def layer_extras(w: W.Workload, args, dev, ctx) -> dict:
     }
 
 
+def power_trace(w: W.Workload) -> str:
+    """Socket power, per-XCD graphics clock and temperatures (amd-smi, sampled about every
+    0.3 s by a child process) while the selective step's attention kernel runs back to back
+    for 10 s, then the merge for 6 s, with idle gaps between: whether a kernel runs at the
+    clock ceiling or the power ceiling."""
+    import subprocess
+    import threading
+    import torch
+    from partitioned_state_reuse_amd import api
+    X = W.make_step(w, 0)
+    dev = torch.device("cuda:0")
+
+    def dev_t(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = dev_t(X.q), dev_t(X.k), dev_t(X.v)
+    sa = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part)
+    sa.step(q, k, v, np.ones((w.n_qb, w.P), np.uint8))
+    mode = "anchor" if w.mode == "anchor" else "distance"
+    planner = api.Planner(w.n_qb, w.P, w.group_offsets, w.local_part, w.anchor_every or 0, w.recompute_groups, mode)
+    mask, _ = planner.next(1)
+    planner.close()
+    valid = np.ones((w.n_qb, w.P), np.uint8)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    samples, phase, done = [], ["idle"], threading.Event()
+
+    def sample():
+        while not done.is_set():
+            t = time.time()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-t", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                d = json.loads(r.stdout)
+                g = (d["gpu_data"] if isinstance(d, dict) else d)[0]
+                clk = [g["clock"][f"gfx_{i}"]["clk"]["value"] for i in range(8) if f"gfx_{i}" in g["clock"]]
+                temp = g.get("temperature", {})
+                hot = temp.get("hotspot", {}).get("value") if isinstance(temp.get("hotspot"), dict) else None
+                mem = temp.get("mem", {}).get("value") if isinstance(temp.get("mem"), dict) else None
+                samples.append((t, phase[0], g["power"]["socket_power"]["value"], clk, hot, mem))
+            except Exception as e:  # no amd-smi or an unexpected format: report and stop sampling
+                samples.append((t, phase[0], None, [], None, repr(e)[:200]))
+                return
+            time.sleep(0.2)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+
+    def run_for(name, seconds, fn, batch):
+        phase[0] = name
+        t0, n = time.time(), 0
+        while time.time() - t0 < seconds:
+            for _ in range(batch):
+                fn()
+            torch.cuda.synchronize()
+            n += batch
+        return (time.time() - t0) / n * 1e3
+
+    time.sleep(2)
+    att_ms = run_for("attention", 10, lambda: api.partition_attention(
+        q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse, cache_valid=valid, stream=stream), 5)
+    phase[0] = "idle"
+    time.sleep(3)
+    mer_ms = run_for("merge", 6, lambda: api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream), 50)
+    phase[0] = "idle"
+    time.sleep(2)
+    done.set()
+    th.join()
+    lines = [f"# {w.name}: attention kernel {att_ms:.2f} ms per launch back to back, merge {mer_ms:.3f} ms",
+             "# time_s  phase       socket_W  gfx_MHz per XCD                                  hotspot_C mem_C"]
+    t_first = samples[0][0] if samples else 0.0
+    prev = None
+    for t, ph, pw, clk, hot, mem in samples:
+        if (ph, pw, clk, hot, mem) == prev:   # amd-smi refreshes about once a second: repeats dropped
+            continue
+        prev = (ph, pw, clk, hot, mem)
+        lines.append(f"{t - t_first:7.2f}  {ph:<10} {str(pw):>8}  {' '.join(f'{c:>5}' for c in clk):<48} {str(hot):>8} {str(mem):>5}")
+    # the sampler refreshes about once a second; steady state: samples at least 1.5 s into a phase
+    for name in ("attention", "merge"):
+        t_start = min((t for t, ph, *_ in samples if ph == name), default=None)
+        sel = [s for s in samples if s[1] == name and t_start is not None and s[0] - t_start >= 1.5 and s[2] is not None]
+        if sel:
+            clk = np.array([s[3] for s in sel], dtype=np.float64)
+            lines.append(f"# {name} steady state ({len(sel)} samples): socket power {np.mean([s[2] for s in sel]):.0f} W, "
+                         f"gfx clock per XCD {' '.join(f'{c:.0f}' for c in clk.mean(axis=0))} MHz "
+                         f"(mean {clk.mean():.0f}), hotspot up to {max(s[4] or 0 for s in sel)} C")
+    return "\n".join(lines)
+
+
 def main() -> int:
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profile":
         print(summarize_profile(sys.argv[2]))
+        return 0
+    if len(sys.argv) in (2, 3) and sys.argv[1] == "--power-trace":
+        # --power-trace [workload]
+        print(power_trace(W.workload(sys.argv[2] if len(sys.argv) == 3 else "video720p")), flush=True)
         return 0
     if len(sys.argv) >= 6 and sys.argv[1] == "--summarize-pmc":
         # --summarize-pmc <workload> <out.json> <FETCH_SIZE dir> <WRITE_SIZE dir> [<SQ dir> ...]
