@@ -285,7 +285,11 @@ def run_trajectory(args, w: "W.Workload") -> dict:
         q, k, v = steps[t]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ev[0].record(stream)
-        did_delta = sa.step(q, k, v, mask, want_importance=anchor, want_delta=t > 0, stream=stream)
+        if args.premerged and not anchor:
+            # reuse step: the reused states pre-merged inside the attention launch
+            did_delta = sa.step_premerged(q, k, v, mask, want_delta=t > 0, stream=stream)
+        else:
+            did_delta = sa.step(q, k, v, mask, want_importance=anchor, want_delta=t > 0, stream=stream)
         ev[1].record(stream)
         imp = sa.importance[0].cpu().numpy() if anchor else None
         dl = sa.delta[0].cpu().numpy() if did_delta else None
@@ -330,6 +334,7 @@ def run_trajectory(args, w: "W.Workload") -> dict:
                    "query_blocks": w.n_qb, "group_size": int(np.diff(w.group_offsets)[0]),
                    "recomputed_groups_per_block": w.recompute_groups, "anchor_every": w.anchor_every,
                    "parallelism": "single GPU"},
+        "reuse_steps": "pre-merged in the attention launch" if args.premerged else "plain",
         "per_step": per_step,
     }
 
@@ -833,6 +838,8 @@ def main() -> int:
     ap.add_argument("--workload", default="video720p", choices=["video720p", "share32", "image_anchor", "longvideo"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share32", action="store_true", help="with the 720p layer: skip the 32-way-share object")
+    ap.add_argument("--premerged", action="store_true",
+                    help="long-video trajectory: reuse steps with the pre-merge in the attention launch")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1 "
