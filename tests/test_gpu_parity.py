@@ -300,3 +300,44 @@ def test_tile_sum_bound_and_maximum_jumps():
     O, lse = oracle.full_attention(qd, kd, vd, 1.0 / sq)
     PT.assert_rows_close(PT.bf16_to_f64(sa.out[0]), O, "tile-sum bound")
     assert np.abs(sa.lse[0].double().cpu().numpy() - lse).max() <= PT.LSE_ABS_TOL
+
+
+def _max_layout(D, seed):
+    """64 query blocks (1 to 17 rows) and 64 partitions (4 to 16 keys, four of them empty),
+    the largest counts the library takes; each block's local partition is a non-empty one."""
+    qs = [1 + (i * 7) % 17 for i in range(64)]
+    ks = [0 if i % 17 == 0 else 4 + (i * 5) % 13 for i in range(64)]
+    qo = [0] + list(np.cumsum(qs))
+    ko = [0] + list(np.cumsum(ks))
+    S_kv = ko[-1]
+    assert qo[-1] <= S_kv
+    local = [i if ks[i] > 0 else i + 1 for i in range(64)]
+    w = _custom(2, D, S_kv, qo, ko, seed=seed)
+    rng = np.random.default_rng(seed)
+    mask = (rng.random((64, 64)) < 0.5).astype(np.uint8)
+    mask[np.arange(64), local] = 1
+    return w, qo, ko, local, mask
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_maximum_blocks_and_partitions(D):
+    w, qo, ko, local, mask = _max_layout(D, seed=91 + D)
+    rows = np.arange(qo[-1])
+    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
+    g = PT.GpuRun(w, q_offsets=qo, kv_offsets=ko, local_part=local)
+    o = PT.OracleRun(w, rows, q_offsets=qo, kv_offsets=ko, local_part=local)
+    ones = np.ones_like(mask)
+    g.step(Xp, ones)
+    o.step(Xp, ones)
+    old = o.local_states()
+    assert g.step(X, mask, want_delta=True, want_importance=True)
+    res = o.step(X, mask)
+    cmp = PT.compare_out(g.out_rows(rows), g.lse_rows(rows), res)
+    _log("64 blocks x 64 partitions", D, cmp)
+    assert cmp.ok(), str(cmp)
+    d_r = oracle.local_change(o.local_states(), old, rows, qo)
+    assert np.allclose(g.sa.delta[0].cpu().numpy(), d_r, rtol=PT.DELTA_REL_TOL)
+    imp = g.sa.importance[0].cpu().numpy()
+    assert np.abs(imp - oracle.importance(res.weights, rows, qo)).max() <= PT.IMP_ABS_TOL
+    empty = [p for p in range(64) if ko[p + 1] == ko[p]]
+    assert len(empty) == 4 and (imp[:, empty] == 0).all()

@@ -188,3 +188,11 @@ def test_premerged_step_share32_full_size_sampled_rows():
 def test_premerged_step_video720p_full_size_sampled_rows():
     w = W.workload("video720p")
     _check_premerged_sampled(w, W.sample_rows(w, tiles_per_block=2, tile=16))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_premerged_step_maximum_blocks_and_partitions(D):
+    """64 query blocks and 64 partitions (the largest counts; every plane bit in use)."""
+    from test_gpu_parity import _max_layout
+    w, qo, ko, local, mask = _max_layout(D, seed=93 + D)
+    _check_premerged_step(w, mask, np.arange(qo[-1]), qo=qo, ko=ko, local=local)
