@@ -48,9 +48,11 @@ def _log(*a):
 
 
 class Fp8Run(PT.GpuRun):
-    def __init__(self, w, B=1):
+    def __init__(self, w, B=1, q_offsets=None, kv_offsets=None, local_part=None):
         self.w = w
-        self.qo, self.ko, self.local = list(w.q_offsets), list(w.kv_offsets), list(w.local_part)
+        self.qo = list(q_offsets if q_offsets is not None else w.q_offsets)
+        self.ko = list(kv_offsets if kv_offsets is not None else w.kv_offsets)
+        self.local = list(local_part if local_part is not None else w.local_part)
         self.sa = api.SelectiveAttention(B, self.qo[-1], self.ko[-1], w.H, w.D, self.qo, self.ko, self.local,
                                          cache_format="fp8")
 
@@ -81,7 +83,9 @@ def check_states(deq, s, O_exact, what):
     bound = state_bound(O_exact)
     err = np.abs(deq - O_exact)
     rel = np.linalg.norm(deq - O_exact) / max(np.linalg.norm(O_exact), 1e-300)
-    _log(f"{what}: max|deq-O|={err.max():.3e} relF={rel:.3e} (max bound ratio {(err / bound).max():.3f})")
+    # empty partitions: state 0 and bound 0 (their slots must decode to exactly 0)
+    ratio = np.divide(err, bound, out=np.zeros_like(err), where=bound > 0)
+    _log(f"{what}: max|deq-O|={err.max():.3e} relF={rel:.3e} (max bound ratio {ratio.max():.3f})")
     assert (err <= bound).all(), f"{what}: {(err > bound).sum()} elements beyond the e4m3 bound"
     assert rel <= E4M3_REL
 
@@ -109,13 +113,18 @@ def check_merge_of_own_codes(g, rows):
     assert (dO <= lim).all(), f"{(dO > lim).sum()} merged elements beyond bf16 rounding"
 
 
-def run_fp8(w, rows, steps=2):
-    """Anchor step on X_prev (all recompute), then the planner's selective step on X."""
-    m_cpp, m_ref, _, _ = PT.masks_from_planners(w)
-    assert np.array_equal(m_cpp, m_ref)
-    ones = np.ones((w.n_qb, w.P), np.uint8)
-    g = Fp8Run(w)
-    o = PT.OracleRun(w, rows)
+def run_fp8(w, rows, steps=2, layout=None):
+    """Anchor step on X_prev (all recompute), then the planner's selective step on X (or, with
+    layout = (q_offsets, kv_offsets, local_part, mask), that split and mask)."""
+    if layout is None:
+        m_cpp, m_ref, _, _ = PT.masks_from_planners(w)
+        assert np.array_equal(m_cpp, m_ref)
+        q_off, kv_off, local = list(w.q_offsets), list(w.kv_offsets), list(w.local_part)
+    else:
+        q_off, kv_off, local, m_cpp = layout
+    ones = np.ones_like(m_cpp)
+    g = Fp8Run(w, q_offsets=q_off, kv_offsets=kv_off, local_part=local)
+    o = PT.OracleRun(w, rows, q_offsets=q_off, kv_offsets=kv_off, local_part=local)
     Xp = W.make_step(w, -1)
     g.step(Xp, ones)
     o.step(Xp, ones)
@@ -126,8 +135,8 @@ def run_fp8(w, rows, steps=2):
         return g, o
     full = len(rows) == w.S_q
     old_exact_local = o.local_states("exact")
-    blk = oracle.block_of_rows(np.asarray(rows), w.q_offsets)
-    old_deq_local = np.stack([deq0[w.local_part[b], j] for j, b in enumerate(blk)])
+    blk = oracle.block_of_rows(np.asarray(rows), q_off)
+    old_deq_local = np.stack([deq0[local[b], j] for j, b in enumerate(blk)])
     X = W.make_step(w, 0)
     did = g.step(X, m_cpp, want_delta=full)
     res = o.step(X, m_cpp)
@@ -146,14 +155,14 @@ def run_fp8(w, rows, steps=2):
     fin = np.isfinite(res.lse)
     assert np.abs(np.where(fin, lse - res.lse, 0.0)).max() <= PT.LSE_ABS_TOL
     if did:
-        new_deq_local = np.stack([deq1[w.local_part[b], j] for j, b in enumerate(blk)])
+        new_deq_local = np.stack([deq1[local[b], j] for j, b in enumerate(blk)])
         d_gpu = g.sa.delta[0].cpu().numpy().astype(np.float64)
-        d_codes = oracle.local_change(new_deq_local, old_deq_local, np.asarray(rows), w.q_offsets)
-        d_exact = oracle.local_change(o.local_states("exact"), old_exact_local, np.asarray(rows), w.q_offsets)
+        d_codes = oracle.local_change(new_deq_local, old_deq_local, np.asarray(rows), q_off)
+        d_exact = oracle.local_change(o.local_states("exact"), old_exact_local, np.asarray(rows), q_off)
         _log("delta fp8 gpu", d_gpu[:4], "of codes", d_codes[:4], "exact", d_exact[:4])
         assert np.allclose(d_gpu, d_codes, rtol=1e-4, atol=0)
         # |delta_fp8 - delta_exact| <= (||q_new|| + ||q_old||) / ||O_old|| + delta_fp8 ||q_old|| / ||O_old||
-        for i in range(w.n_qb):
+        for i in range(len(q_off) - 1):
             sel = blk == i
             on = np.linalg.norm(old_exact_local[sel])
             qn = np.linalg.norm(new_deq_local[sel] - o.local_states("exact")[sel])
@@ -246,3 +255,12 @@ def test_fp8_longvideo_trajectory_reduced_grid():
         cp.observe(t, imp, d)
     cp.close()
     _log("worst bound ratio over the trajectory", worst)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_maximum_blocks_and_partitions(D):
+    """64 query blocks and 64 partitions, four of them empty (their slots hold scale 0 and
+    codes 0), D = 64 and 128."""
+    from test_gpu_parity import _max_layout
+    w, qo, ko, local, mask = _max_layout(D, seed=95 + D)
+    run_fp8(w, np.arange(qo[-1]), layout=(qo, ko, local, mask))
