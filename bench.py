@@ -507,7 +507,7 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
         f"finalize {fin_ms:.4f} ms")
     traffic = measured_traffic(w.name)
     attn_counters = measured_counters(w.name)
-    merge_kernel = f"state_merge_kernel<128, {16 if w.P <= 16 else 32 if w.P <= 32 else 64}>"
+    merge_kernel = f"state_merge_kernel<128, {16 if w.P <= 16 else 32 if w.P <= 32 else 64}, false>"
     res = {
         "ms_per_step": round(ms_step, 4),
         "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
