@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import math
 import os
 import sys
@@ -69,6 +70,27 @@ def measured_counters(workload: str) -> dict:
     if rec.get("source_sha256") != kernel_source_sha256():
         return {}
     return rec.get("attention_counters", {})
+
+
+def measured_power(workload: str) -> dict:
+    """Steady-state socket power and graphics clock of the attention kernel and of the merge
+    from the committed power trace of this workload (bench.py --power-trace); empty when the
+    kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"power_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    m = re.search(r"^# source_sha256 ([0-9a-f]+)$", text, flags=re.M)
+    if not m or m.group(1) != kernel_source_sha256():
+        return {}
+    out = {"source": f"profiles/power_{workload}.txt"}
+    for name in ("attention", "merge"):
+        r = re.search(rf"^# {name} steady state \((\d+) samples\): socket power (\d+) W, gfx clock per XCD ([\d ]+) MHz "
+                      rf"\(mean (\d+)\)", text, flags=re.M)
+        if r:
+            out[name] = {"socket_w": int(r.group(2)), "gfx_mhz_per_xcd": [int(x) for x in r.group(3).split()],
+                         "gfx_mhz_mean": int(r.group(4))}
+    return out
 
 
 def measured_traffic(workload: str) -> dict:
@@ -522,7 +544,8 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
                      "kernel": "partition_attention_kernel<128, false>", "ms": round(attn_ms, 4),
                      "algorithmic_flop": flop, "counters": attn_counters or None,
                      "frac_of_clock_peak": (round(attn_tflops / attn_counters["peak_tflops_at_that_clock"], 4)
-                                            if attn_counters else None)},
+                                            if attn_counters else None),
+                     "power": measured_power(w.name) or None},
         "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
                            "traffic": traffic.get("dit::" + merge_kernel),
@@ -798,7 +821,8 @@ def power_trace(w: W.Workload) -> str:
     time.sleep(2)
     done.set()
     th.join()
-    lines = [f"# {w.name}: attention kernel {att_ms:.2f} ms per launch back to back, merge {mer_ms:.3f} ms",
+    lines = [f"# source_sha256 {kernel_source_sha256()}",
+             f"# {w.name}: attention kernel {att_ms:.2f} ms per launch back to back, merge {mer_ms:.3f} ms",
              "# time_s  phase       socket_W  gfx_MHz per XCD                                  hotspot_C mem_C"]
     t_first = samples[0][0] if samples else 0.0
     prev = None
