@@ -200,8 +200,8 @@ def summarize_pmc(workload: str, out_json: str, fetch_dir: str, write_dir: str, 
 
     def copy_reading(runs, counter):
         # the bench's 4 GiB device copy runs four times with identical readings; the other
-        # copies of a run (cache clones, uploads) have other sizes: take the value that
-        # occurs most often (within 0.1%)
+        # copies of a run (cache clones, uploads, sampled-row gathers) are smaller: take the
+        # largest value that occurs at least three times (within 0.1%)
         vals = sorted(d[counter] for (n, _), r in runs.items() if "copyBuffer" in n
                       for d in r["dispatch"].values() if counter in d)
         groups = []
@@ -210,7 +210,7 @@ def summarize_pmc(workload: str, out_json: str, fetch_dir: str, write_dir: str, 
                 groups[-1].append(x)
             else:
                 groups.append([x])
-        best = max(groups, key=len)
+        best = max((g for g in groups if len(g) >= 3), key=lambda g: g[0])
         return float(np.mean(best)), len(best)
 
     (fetch_copy, nf), (write_copy, nw) = copy_reading(fetch, "FETCH_SIZE"), copy_reading(write, "WRITE_SIZE")
@@ -244,40 +244,56 @@ def summarize_pmc(workload: str, out_json: str, fetch_dir: str, write_dir: str, 
         lines.append(f"#   {n:<46} FETCH {k['fetch_kib']:>12.0f} KiB x {rf:.4f} = {k['hbm_read_bytes'] / 1e9:8.3f} GB read, "
                      f"WRITE {k['write_kib']:>12.0f} KiB x {wf:.4f} = {k['hbm_write_bytes'] / 1e9:8.3f} GB written")
     if sq_dirs:
-        sq = {}
-        for dpath in sq_dirs:
-            for key, r in read_pmc(dpath).items():
-                if key[0] == "dit::partition_attention_kernel<128, false>" and key[1] == attn_grid:
-                    for c in {c for d in r["dispatch"].values() for c in d if not c.startswith("_")}:
-                        sq[c] = pmc_mean(r, c)
-                    sq["_ns"] = pmc_mean(r, "_ns")
-        clocks = sq["GRBM_GUI_ACTIVE"] / 8
-        ghz = clocks / sq["_ns"]
-        busy = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * clocks)
-        counters = {"kernel": "dit::partition_attention_kernel<128, false>", "clock_ghz_under_load": round(ghz, 3),
-                    "mfma_busy_frac": round(busy, 4), "peak_tflops_at_that_clock": round(PEAK_BF16_TFLOPS * ghz / 2.4, 1),
-                    "commands": "rocprofv3 --pmc <SQ counters> -- python3 -u bench.py --steps 2 --warmup 0 "
-                                "--no-cpu-baseline (two passes)"}
-        if "SQ_WAIT_ANY" in sq:
-            counters["waves_waiting_frac"] = round(sq["SQ_WAIT_ANY"] / sq["SQ_WAVE_CYCLES"], 4)
-        if "SQ_LDS_IDX_ACTIVE" in sq:
-            counters["lds_indexed_active_frac"] = round(sq["SQ_LDS_IDX_ACTIVE"] / (256 * clocks), 4)
-        if "SQ_VALU_MFMA_COEXEC_CYCLES" in sq:
-            counters["mfma_valu_coexec_frac"] = round(sq["SQ_VALU_MFMA_COEXEC_CYCLES"] / (1024 * clocks), 4)
-        if "SQ_INSTS_VALU" in sq:
-            counters["valu_instructions_per_mfma"] = round(sq["SQ_INSTS_VALU"] / sq["SQ_INSTS_MFMA"], 3)
-        if "TCC_HIT_sum" in sq:
-            counters["l2_hit_frac"] = round(sq["TCC_HIT_sum"] / (sq["TCC_HIT_sum"] + sq["TCC_MISS_sum"]), 4)
-        rec["attention_counters"] = counters
-        lines.append(f"# SQ counters of dit::partition_attention_kernel<128, false> (mean over {attn_grid}-thread dispatches):")
-        for c in sorted(k for k in sq if not k.startswith("_")):
-            lines.append(f"#   {c:<28} {sq[c]:.4e}")
-        lines.append(f"#   dispatch duration under the counters {sq['_ns'] / 1e6:.2f} ms; GRBM_GUI_ACTIVE / 8 XCDs = "
-                     f"{clocks:.4e} clocks -> {ghz:.2f} GHz; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x clocks)"
-                     f" = {busy:.1%}")
-        for k, v in counters.items():
-            if k.endswith("_frac") or k.endswith("_per_mfma") or k.endswith("_ghz_under_load"):
-                lines.append(f"#   {k} {v}")
+        def sq_of(match):
+            sq = {}
+            for dpath in sq_dirs:
+                for key, r in read_pmc(dpath).items():
+                    if match(*key):
+                        for c in {c for d in r["dispatch"].values() for c in d if not c.startswith("_")}:
+                            sq[c] = pmc_mean(r, c)
+                        sq["_ns"] = pmc_mean(r, "_ns")
+            return sq
+
+        def figures(kernel, sq):
+            clocks = sq["GRBM_GUI_ACTIVE"] / 8
+            ghz = clocks / sq["_ns"]
+            busy = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * clocks)
+            counters = {"kernel": kernel, "clock_ghz_under_load": round(ghz, 3),
+                        "mfma_busy_frac": round(busy, 4), "peak_tflops_at_that_clock": round(PEAK_BF16_TFLOPS * ghz / 2.4, 1),
+                        "commands": "rocprofv3 --pmc <SQ counters> -- python3 -u bench.py --steps 2 --warmup 0 "
+                                    "--no-cpu-baseline (two passes)"}
+            if "SQ_WAIT_ANY" in sq:
+                counters["waves_waiting_frac"] = round(sq["SQ_WAIT_ANY"] / sq["SQ_WAVE_CYCLES"], 4)
+            if "SQ_LDS_IDX_ACTIVE" in sq:
+                counters["lds_indexed_active_frac"] = round(sq["SQ_LDS_IDX_ACTIVE"] / (256 * clocks), 4)
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in sq:
+                counters["mfma_valu_coexec_frac"] = round(sq["SQ_VALU_MFMA_COEXEC_CYCLES"] / (1024 * clocks), 4)
+            if "SQ_INSTS_VALU" in sq:
+                counters["valu_instructions_per_mfma"] = round(sq["SQ_INSTS_VALU"] / sq["SQ_INSTS_MFMA"], 3)
+            if "TCC_HIT_sum" in sq:
+                counters["l2_hit_frac"] = round(sq["TCC_HIT_sum"] / (sq["TCC_HIT_sum"] + sq["TCC_MISS_sum"]), 4)
+            lines.append(f"# SQ counters of {kernel} (mean over its dispatches of this workload):")
+            for c in sorted(k for k in sq if not k.startswith("_")):
+                lines.append(f"#   {c:<28} {sq[c]:.4e}")
+            lines.append(f"#   dispatch duration under the counters {sq['_ns'] / 1e6:.2f} ms; GRBM_GUI_ACTIVE / 8 XCDs = "
+                         f"{clocks:.4e} clocks -> {ghz:.2f} GHz; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x clocks)"
+                         f" = {busy:.1%}")
+            for k, v in counters.items():
+                if k.endswith("_frac") or k.endswith("_per_mfma") or k.endswith("_ghz_under_load"):
+                    lines.append(f"#   {k} {v}")
+            return counters
+
+        plain_name = "dit::partition_attention_kernel<128, false>"
+        pre_name = "dit::partition_attention_premerge_kernel<128>"
+        sq_plain = sq_of(lambda n, g: n == plain_name and g == attn_grid)
+        sq_pre = sq_of(lambda n, g: n == pre_name and attn_grid < g <= attn_grid + (1 << 20))
+        # the bench step's attention launch: the one with the reuse pre-merge when the step reuses
+        if sq_pre:
+            rec["attention_counters"] = figures(pre_name, sq_pre)
+            if sq_plain:
+                rec["plain_attention_counters"] = figures(plain_name, sq_plain)
+        elif sq_plain:
+            rec["attention_counters"] = figures(plain_name, sq_plain)
     with open(out_json, "w") as f:
         json.dump(rec, f, indent=1)
     return "\n".join(lines)
@@ -307,11 +323,9 @@ def run_trajectory(args, w: "W.Workload") -> dict:
         q, k, v = steps[t]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ev[0].record(stream)
-        if args.premerged and not anchor:
-            # reuse step: the reused states pre-merged inside the attention launch
-            did_delta = sa.step_premerged(q, k, v, mask, want_delta=t > 0, stream=stream)
-        else:
-            did_delta = sa.step(q, k, v, mask, want_importance=anchor, want_delta=t > 0, stream=stream)
+        # (a reuse step merges the reused states inside the attention launch; an anchor step,
+        # which computes the importance, merges all states after it)
+        did_delta = sa.step(q, k, v, mask, want_importance=anchor, want_delta=t > 0, stream=stream)
         ev[1].record(stream)
         imp = sa.importance[0].cpu().numpy() if anchor else None
         dl = sa.delta[0].cpu().numpy() if did_delta else None
@@ -356,7 +370,6 @@ def run_trajectory(args, w: "W.Workload") -> dict:
                    "query_blocks": w.n_qb, "group_size": int(np.diff(w.group_offsets)[0]),
                    "recomputed_groups_per_block": w.recompute_groups, "anchor_every": w.anchor_every,
                    "parallelism": "single GPU"},
-        "reuse_steps": "pre-merged in the attention launch" if args.premerged else "plain",
         "per_step": per_step,
     }
 
@@ -473,40 +486,64 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     valid = np.ones((w.n_qb, w.P), np.uint8)
 
-    def one_step(t, events=None):
+    def one_step(t, events=None, plain=False):
+        """One step as dit_attn_partitioned runs it: on a step that reuses states, the reused
+        states are merged inside the attention launch into out / lse and a masked merge combines
+        the fresh states with them in place; otherwise (or with plain) the attention launch and
+        then the merge of all P states."""
         mask, _ = planner.next(t)
+        pre = not plain and not mask.all()
         if events:
             events[0].record(stream)
-        api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
-                                local_part=w.local_part, cache_valid=valid, workspace=sa.workspace,
-                                stream=stream)
+        if pre:
+            api.partition_attention_premerge(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
+                                             sa.out, sa.lse, workspace=sa.workspace, local_part=w.local_part,
+                                             cache_valid=valid, stream=stream)
+        else:
+            api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
+                                    local_part=w.local_part, cache_valid=valid, workspace=sa.workspace,
+                                    stream=stream)
         if events:
             events[1].record(stream)
-        api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
+        if pre:
+            api.state_merge_masked(sa.cache_o, sa.cache_lse, w.q_offsets, mask, sa.out, sa.lse, extra_o=sa.out,
+                                   extra_lse=sa.lse, stream=stream)
+        else:
+            api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
         if events:
             events[2].record(stream)
         api.local_change_finalize(sa.workspace, 1, w.S_q, w.H, w.D, w.q_offsets, sa.delta, stream=stream)
         if events:
             events[3].record(stream)
-        return mask
+        return mask, pre
 
-    for t in range(args.warmup):
-        mask = one_step(t + 1)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for t in range(args.steps):
-        mask = one_step(t + 1, ev[t])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_step = wall / max(args.steps, 1) * 1e3
-    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    merge_in_step_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    fin_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    def timed(plain):
+        for t in range(args.warmup):
+            one_step(t + 1, plain=plain)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for t in range(args.steps):
+            mask, pre = one_step(t + 1, ev[t], plain=plain)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        return (mask, pre, wall / max(args.steps, 1) * 1e3, float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+                float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+                float(np.mean([e[2].elapsed_time(e[3]) for e in ev])))
+
+    mask, pre, ms_step, attn_ms, merge_in_step_ms, fin_ms = timed(False)
     # the GPU's output of the step, for the parity check beside the oracle
     rows = np.arange(w.S_q) if w.S_q <= 4096 else W.sample_rows(w, tiles_per_block=2, tile=128)
     ridx = torch.as_tensor(rows, device=dev)
     gpu_out = W.to_f64(sa.out[0, ridx].view(torch.int16).cpu().numpy().view(np.uint16))
     gpu_lse = sa.lse[0][:, ridx].double().cpu().numpy()
+    # the same steps with the plain sequence (attention launch, then the merge of all P states)
+    plain = None
+    if pre:
+        _, _, p_ms, p_attn_ms, p_merge_ms, _ = timed(True)
+        p_out = W.to_f64(sa.out[0, ridx].view(torch.int16).cpu().numpy().view(np.uint16))
+        plain = {"ms_per_step": round(p_ms, 4), "attention_ms": round(p_attn_ms, 4),
+                 "merge_in_step_ms": round(p_merge_ms, 4), "kernel": "partition_attention_kernel<128, false>",
+                 "max_abs_diff_vs_step_out": float(np.abs(p_out - gpu_out).max())}
 
     # the merge alone on a cold cache (rotating over copies of the cache); the importance
     # variant of anchor steps on the same copies
@@ -523,12 +560,21 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
     mbytes = merge_bytes(w)
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
     merge_gbs = mbytes / (merge_ms * 1e-3) / 1e9
-    log(f"[bench] {w.name}: step {ms_step:.3f} ms  attention {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s)  "
-        f"merge {merge_ms:.3f} ms cold ({merge_gbs:.0f} GB/s; in the step {merge_in_step_ms:.3f} ms; with importance "
-        f"{anchor_merge_ms:.3f} ms)  "
-        f"finalize {fin_ms:.4f} ms")
+    attn_kernel = "partition_attention_premerge_kernel<128>" if pre else "partition_attention_kernel<128, false>"
+    log(f"[bench] {w.name}: step {ms_step:.3f} ms  attention launch {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s"
+        f"{', with the reuse pre-merge' if pre else ''})  {'final combine' if pre else 'merge'} in the step "
+        f"{merge_in_step_ms:.3f} ms  merge of all planes {merge_ms:.3f} ms cold ({merge_gbs:.0f} GB/s; with importance "
+        f"{anchor_merge_ms:.3f} ms)  finalize {fin_ms:.4f} ms")
+    if plain:
+        plain["value"] = round(flop / (plain["ms_per_step"] * 1e-3) / 1e12, 2)
+        plain["attention_tflops"] = round(flop / (plain["attention_ms"] * 1e-3) / 1e12, 2)
+        plain["attention_frac"] = round(plain["attention_tflops"] / PEAK_BF16_TFLOPS, 4)
+        log(f"[bench] {w.name}: plain step {plain['ms_per_step']:.3f} ms  attention {plain['attention_ms']:.3f} ms "
+            f"({plain['attention_tflops']:.1f} TFLOP/s)  merge in the step {plain['merge_in_step_ms']:.3f} ms")
     traffic = measured_traffic(w.name)
     attn_counters = measured_counters(w.name)
+    if attn_counters and attn_counters.get("kernel") != "dit::" + attn_kernel:
+        attn_counters = {}
     merge_kernel = f"state_merge_kernel<128, {16 if w.P <= 16 else 32 if w.P <= 32 else 64}, false>"
     res = {
         "ms_per_step": round(ms_step, 4),
@@ -540,8 +586,8 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic.get("dit::partition_attention_kernel<128, false>"),
-                     "kernel": "partition_attention_kernel<128, false>", "ms": round(attn_ms, 4),
+                     "traffic": traffic.get("dit::" + attn_kernel),
+                     "kernel": attn_kernel, "ms": round(attn_ms, 4),
                      "algorithmic_flop": flop, "counters": attn_counters or None,
                      "frac_of_clock_peak": (round(attn_tflops / attn_counters["peak_tflops_at_that_clock"], 4)
                                             if attn_counters else None),
@@ -549,79 +595,29 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
         "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
                            "traffic": traffic.get("dit::" + merge_kernel),
-                           "kernel": merge_kernel, "ms": round(merge_ms, 4), "ms_in_step": round(merge_in_step_ms, 4),
+                           "kernel": merge_kernel, "ms": round(merge_ms, 4),
+                           "in_step": ("final combine (masked merge of the fresh planes and the pre-merged state)"
+                                       if pre else "this merge"), "ms_in_step": round(merge_in_step_ms, 4),
                            "algorithmic_bytes": mbytes,
                            "timing": "median over launches rotating over copies of the cache (cold MALL)",
                            "anchor_ms": round(anchor_merge_ms, 4),
                            "anchor_what": "the same merge with the importance partials and their fixed-order finish"},
         "local_change_finalize_ms": round(fin_ms, 5),
+        "plain_step": plain,
     }
+    plain_ms = plain["ms_per_step"] if plain else ms_step
     ctx = {"X": X, "Xp": Xp, "mask": mask, "rows": rows, "gpu_out": gpu_out, "gpu_lse": gpu_lse,
            "q": q, "k": k, "v": v, "sa": sa, "planner": planner, "flop": flop, "ms_step": ms_step,
-           "merge_ms": merge_ms}
+           "plain_ms_step": plain_ms, "merge_ms": merge_ms}
     if extras:
         res.update(layer_extras(w, args, dev, ctx))
-    else:
+    elif pre:
         ov_ms = overlapped_step_ms(args, ctx)
-        log(f"[bench] {w.name}: overlapped step {ov_ms:.3f} ms (plain {ms_step:.3f})")
-        res["overlap_two_streams"] = {"ms_per_step": round(ov_ms, 4), "plain_ms_per_step": round(ms_step, 4),
+        log(f"[bench] {w.name}: two-stream step {ov_ms:.3f} ms (plain {plain_ms:.3f})")
+        res["overlap_two_streams"] = {"ms_per_step": round(ov_ms, 4), "plain_ms_per_step": round(plain_ms, 4),
                                       "value": round(flop / (ov_ms * 1e-3) / 1e12, 2)}
-        res["reuse_in_attention_tail"] = premerged_step(w, args, ctx)
     planner.close()
     return res, ctx
-
-
-def premerged_step(w: W.Workload, args, ctx) -> dict:
-    """The step with the reuse work inside the attention launch: the launch's last
-    workgroups pre-merge the reused states in the slots the attention work leaves as it
-    drains; then the fresh states and that partial are merged.  Same planner, work list,
-    local change and inputs as the plain step."""
-    import torch
-    from partitioned_state_reuse_amd import api
-    q, k, v, sa, planner = ctx["q"], ctx["k"], ctx["v"], ctx["sa"], ctx["planner"]
-    stream = torch.cuda.current_stream()
-    valid = np.ones((w.n_qb, w.P), np.uint8)
-    partial_o = torch.empty_like(sa.out)
-    partial_lse = torch.empty_like(sa.lse)
-
-    def one(t, e=None):
-        m_t, _ = planner.next(t)
-        if e:
-            e[0].record(stream)
-        api.partition_attention_premerge(q, k, v, w.q_offsets, w.kv_offsets, m_t, sa.cache_o, sa.cache_lse,
-                                         partial_o, partial_lse, workspace=sa.workspace, local_part=w.local_part,
-                                         cache_valid=valid, stream=stream)
-        if e:
-            e[1].record(stream)
-        api.state_merge_masked(sa.cache_o, sa.cache_lse, w.q_offsets, m_t, sa.out, sa.lse, extra_o=partial_o,
-                               extra_lse=partial_lse, stream=stream)
-        if e:
-            e[2].record(stream)
-        api.local_change_finalize(sa.workspace, 1, w.S_q, w.H, w.D, w.q_offsets, sa.delta, stream=stream)
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for t in range(args.warmup):
-        one(t + 1)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(args.steps):
-        one(t + 1, ev[t])
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
-    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    fin_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    # the same inputs and mask as the plain step: on the rows the parity check samples, the
-    # outputs agree to bf16 rounding
-    ridx = torch.as_tensor(ctx["rows"], device=q.device)
-    got = W.to_f64(sa.out[0, ridx].view(torch.int16).cpu().numpy().view(np.uint16))
-    diff = float(np.abs(got - ctx["gpu_out"]).max())
-    del partial_o, partial_lse
-    log(f"[bench] {w.name}: step with the pre-merge in the attention launch {ms:.3f} ms (plain {ctx['ms_step']:.3f}): "
-        f"attention + pre-merge {attn_ms:.3f} ms, final combine {fin_ms:.3f} ms")
-    return {"ms_per_step": round(ms, 4), "plain_ms_per_step": round(ctx["ms_step"], 4),
-            "value": round(ctx["flop"] / (ms * 1e-3) / 1e12, 2),
-            "attention_with_premerge_ms": round(attn_ms, 4), "final_combine_ms": round(fin_ms, 4),
-            "max_abs_diff_vs_plain_out": diff}
 
 
 def overlapped_step_ms(args, ctx) -> float:
@@ -675,7 +671,6 @@ def layer_extras(w: W.Workload, args, dev, ctx) -> dict:
         f"{enqueue_us:.1f} us")
 
     ov_ms = overlapped_step_ms(args, ctx)
-    tail = premerged_step(w, args, ctx)
     # dynamic group compose of the P cached states into the groups
     go = w.group_offsets
     G = len(go) - 1
@@ -691,7 +686,7 @@ def layer_extras(w: W.Workload, args, dev, ctx) -> dict:
     comp_ms = c0_.elapsed_time(c1_) / 5
     comp_bytes = float(w.S_q * w.H * (w.P + G) * (2 * w.D + 4))
     del comp_o, comp_l
-    log(f"[bench] overlapped step {ov_ms:.3f} ms (plain {ctx['ms_step']:.3f}); group compose {comp_ms:.3f} ms "
+    log(f"[bench] two-stream step {ov_ms:.3f} ms (plain {ctx['plain_ms_step']:.3f}); group compose {comp_ms:.3f} ms "
         f"({comp_bytes / (comp_ms * 1e-3) / 1e9:.0f} GB/s)")
 
     # compressed (fp8 e4m3 + per-row-head scale) state cache: same step on its own cache
@@ -734,9 +729,8 @@ def layer_extras(w: W.Workload, args, dev, ctx) -> dict:
     log(f"[bench] fp8 cache step {fp8_ms:.3f} ms: attention {fp8_attn_ms:.3f} ms, merge {fp8_merge_ms:.3f} ms "
         f"({fp8_bytes / (fp8_merge_ms * 1e-3) / 1e9:.0f} GB/s)")
     return {
-        "overlap_two_streams": {"ms_per_step": round(ov_ms, 4), "plain_ms_per_step": round(ctx["ms_step"], 4),
+        "overlap_two_streams": {"ms_per_step": round(ov_ms, 4), "plain_ms_per_step": round(ctx["plain_ms_step"], 4),
                                 "value": round(flop / (ov_ms * 1e-3) / 1e12, 2)},
-        "reuse_in_attention_tail": tail,
         "group_compose": {"ms": round(comp_ms, 4), "gbs": round(comp_bytes / (comp_ms * 1e-3) / 1e9, 1),
                           "frac": round(comp_bytes / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                           "algorithmic_bytes": comp_bytes, "planes": f"{w.P} -> {len(w.group_offsets) - 1}"},
@@ -862,8 +856,6 @@ def main() -> int:
     ap.add_argument("--workload", default="video720p", choices=["video720p", "share32", "image_anchor", "longvideo"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share32", action="store_true", help="with the 720p layer: skip the 32-way-share object")
-    ap.add_argument("--premerged", action="store_true",
-                    help="long-video trajectory: reuse steps with the pre-merge in the attention launch")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1 "

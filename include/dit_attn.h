@@ -98,6 +98,11 @@ size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P);
  * One selective attention step (partition attention, cache update, merge, and optionally
  * importance and local change).  Equivalent to dit_partition_attention, then
  * dit_state_merge, then dit_importance / dit_local_change_finalize when requested.
+ * On a step that reuses some slot and asks for no importance, when a workspace is given,
+ * the merge of the reused states runs inside the attention launch, into out / lse (as
+ * dit_partition_attention_premerge does), and dit_state_merge_masked then combines the
+ * fresh states with that partial state in place: the same result up to the rounding order
+ * of the fp32 merge (DiTango, technical summary, "Methodology §2, Pipeline Orchestration").
  *
  *   softmax_scale      > 0, or <= 0 for 1/sqrt(D)
  *   local_part         host [n_qb] or NULL: each block's own partition.  When given, the
@@ -109,8 +114,8 @@ size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P);
  *                      states the local slots held before this call.  Needs local_part and
  *                      a workspace; with cache_valid given the local slots must be valid.
  *   workspace          device, >= dit_attn_workspace_bytes(...) when delta_out or
- *                      importance_out is given, else may be NULL.  Contents on entry are
- *                      ignored.  The importance is computed inside the merge (partial sums
+ *                      importance_out is given, else may be NULL (then the reused states are
+ *                      merged after the attention launch).  Contents on entry are ignored.  The importance is computed inside the merge (partial sums
  *                      per merge workgroup, finished in a fixed order).  Calls that share a
  *                      workspace must not run at the same time.
  */
@@ -140,10 +145,12 @@ int dit_attn_partitioned(const void *q, const void *k, const void *v,
  *   - delta_out given and B * (ceil(S_q / 128) + n_qb) * H * 8 bytes (the local-change
  *     partials) above DIT_SCRATCH_BYTES: DIT_ERR_WORKSPACE (e.g. B = 1, H = 40 allows about
  *     3,270 query tiles of 128 rows plus blocks, S_q up to ~410,000 rows).
- *   - The array holds the local-change partial sums; the importance, when asked for, is
- *     taken in a second pass over the stored lse planes (no partials kept).  The array keeps
- *     the last call's contents; every entry a call reads is written by the same call, so
- *     nothing needs clearing.  Calls that overlap on one GPU (on different streams, or from
+ *   - The array holds the local-change partial sums and, when delta_out is given, the chunk
+ *     counter of the in-launch merge of the reused states (cleared by the call itself);
+ *     without delta_out the reused states are merged after the attention launch.  The
+ *     importance, when asked for, is taken in a second pass over the stored lse planes (no
+ *     partials kept).  The array keeps the last call's contents; every entry a call reads is
+ *     written (or cleared) by the same call.  Calls that overlap on one GPU (on different streams, or from
  *     different threads) share the array and race: serialise them.
  *   - Unlike the other calls this one keeps state across calls (the per-device address).
  */

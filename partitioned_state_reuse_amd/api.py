@@ -435,10 +435,11 @@ class SelectiveAttention:
                                       stream=stream)
             self.valid |= recompute
             return do_delta
+        # the workspace always goes along: on a reuse step without importance the library merges
+        # the reused states inside the attention launch (its chunk counter lives there)
         attn_partitioned(q, k, v, self.q_offsets, self.kv_offsets, recompute, self.cache_o, self.cache_lse,
                          self.out, self.lse, local_part=self.local_part, cache_valid=self.valid, scale=scale,
                          importance_out=self.importance if want_importance else None,
-                         delta_out=self.delta if do_delta else None,
-                         workspace=self.workspace if (do_delta or want_importance) else None, stream=stream)
+                         delta_out=self.delta if do_delta else None, workspace=self.workspace, stream=stream)
         self.valid |= recompute
         return do_delta

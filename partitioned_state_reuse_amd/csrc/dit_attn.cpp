@@ -166,6 +166,43 @@ float scale_log2_of(float softmax_scale, int D) {
   return s * 1.4426950408889634f;
 }
 
+// The reuse work of an attention launch (the merge of each block's reused planes into
+// pre_o / pre_lse by workgroups dispatched after the attention items): its description, with
+// the chunk counter at the start of the workspace's second region.  The workspace must hold
+// claim_offset(...) + 4 bytes.
+size_t claim_offset(int B, int S_q, int H, int n_qb) { return imp_ws_offset(B, S_q, H, n_qb); }
+
+int make_tail(const AttnDesc &desc, const uint8_t *recompute, int B, int S_q, int H, int D, int n_qb, int P,
+              void *pre_o, float *pre_lse, void *workspace, dit::TailMerge &tm) {
+  memset(&tm, 0, sizeof(tm));
+  tm.pre_o = pre_o;
+  tm.pre_lse = pre_lse;
+  tm.claim = (uint32_t *)((char *)workspace + claim_offset(B, S_q, H, n_qb));
+  for (int i = 0; i < n_qb; ++i)
+    for (int p = 0; p < P; ++p)
+      if (!recompute[i * P + p]) tm.reuse_mask[i] |= (uint64_t)1 << p;
+  // chunks: about 8 per resident workgroup slot of the device, 1 to 16 passes each
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return DIT_ERR_HIP;
+  const int64_t slots = std::max<int64_t>(1, (int64_t)cus * dit::kMinBlocks);
+  const int64_t rpw = 256 / (D / 8);
+  const int64_t passes = ((int64_t)B * S_q * H + rpw - 1) / rpw;
+  const int64_t chunk_passes = std::min<int64_t>(16, std::max<int64_t>(1, passes / (8 * slots)));
+  const int64_t n_chunks = (passes + chunk_passes - 1) / chunk_passes;
+  const int64_t n_attn = (int64_t)B * H * desc.items_per_head;
+  const int64_t n_tail = std::min(n_chunks, slots);
+  // every tail workgroup ends with one failed claim: the counter reaches n_chunks + n_tail
+  if ((n_attn + n_tail) * (dit::kWaves * 64) > (int64_t)UINT32_MAX || n_chunks + n_tail > (int64_t)UINT32_MAX)
+    return DIT_ERR_SHAPE;
+  tm.n_attn_wg = (int32_t)n_attn;
+  tm.n_tail_wg = (int32_t)n_tail;
+  tm.n_chunks = (int32_t)n_chunks;
+  tm.chunk_passes = (int32_t)chunk_passes;
+  return DIT_OK;
+}
+
 // One selective step (dit_attn_partitioned) on a given workspace.  fused_importance: the
 // importance comes from the merge's partials (in the workspace); otherwise from a second
 // pass over the stored lse planes, which needs no workspace.
@@ -189,13 +226,40 @@ int run_partitioned(const void *q, const void *k, const void *v, int B, int S_q,
         (st = check_importance(D, false, B, S_q, H, P, q_offsets, n_qb, workspace, workspace_bytes, bd, imp_part)))
       return st;
     hipStream_t s = as_stream(stream);
-    if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse,
-                                        want_delta ? (float *)workspace : nullptr, desc,
-                                        scale_log2_of(softmax_scale, D), s) != hipSuccess)
-      return DIT_ERR_HIP;
-    if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, false, fuse ? &bd : nullptr, imp_part,
-                                importance_out, s) != hipSuccess)
-      return DIT_ERR_HIP;
+    // A step that reuses some slot and asks for no importance (which the full merge computes)
+    // takes the reused states' merge into the attention launch, into out / lse, when the
+    // workspace can hold the chunk counter; a masked merge then combines the fresh states with
+    // that partial state in place.
+    bool any_reuse = false;
+    for (int e = 0; e < n_qb * P && !any_reuse; ++e) any_reuse = recompute[e] == 0;
+    if (importance_out == nullptr && any_reuse && workspace != nullptr &&
+        workspace_bytes >= claim_offset(B, S_q, H, n_qb) + sizeof(uint32_t)) {
+      dit::TailMerge tm;
+      if ((st = make_tail(desc, recompute, B, S_q, H, D, n_qb, P, out, lse, workspace, tm))) return st;
+      if (dit::launch_partition_attention_premerge(D, q, k, v, cache_o, cache_lse,
+                                                   want_delta ? (float *)workspace : nullptr, desc,
+                                                   scale_log2_of(softmax_scale, D), tm, s) != hipSuccess)
+        return DIT_ERR_HIP;
+      dit::MergeSelect sel;
+      memset(&sel, 0, sizeof(sel));
+      sel.n_qb = n_qb;
+      sel.has_extra = 1;
+      for (int i = 0; i <= n_qb; ++i) sel.q_off[i] = q_offsets[i];
+      for (int i = 0; i < n_qb; ++i)
+        for (int p = 0; p < P; ++p)
+          if (recompute[i * P + p]) sel.plane_mask[i] |= (uint64_t)1 << p;
+      if (dit::launch_state_merge_masked(D, P, cache_o, cache_lse, out, lse, sel, out, lse, B, S_q, H, s) !=
+          hipSuccess)
+        return DIT_ERR_HIP;
+    } else {
+      if (dit::launch_partition_attention(D, false, q, k, v, cache_o, nullptr, cache_lse,
+                                          want_delta ? (float *)workspace : nullptr, desc,
+                                          scale_log2_of(softmax_scale, D), s) != hipSuccess)
+        return DIT_ERR_HIP;
+      if (dit::launch_state_merge(D, P, cache_o, cache_lse, out, lse, B, S_q, H, false, fuse ? &bd : nullptr,
+                                  imp_part, importance_out, s) != hipSuccess)
+        return DIT_ERR_HIP;
+    }
     if (importance_out && !fuse &&
         dit::launch_importance(cache_lse, lse, B, S_q, H, P, bd, importance_out, s) != hipSuccess)
       return DIT_ERR_HIP;
@@ -268,37 +332,11 @@ int dit_partition_attention_premerge(const void *q, const void *k, const void *v
     int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
                         cache_valid, cache_o, cache_lse, want_delta, workspace, workspace_bytes, desc);
     if (st) return st;
-    // the claim counter sits at the start of the workspace's second region
+    // the chunk counter sits at the start of the workspace's second region
     if (!workspace) return DIT_ERR_WORKSPACE;
-    const size_t claim_off = imp_ws_offset(B, S_q, H, n_qb);
-    if (workspace_bytes < claim_off + sizeof(uint32_t)) return DIT_ERR_WORKSPACE;
+    if (workspace_bytes < claim_offset(B, S_q, H, n_qb) + sizeof(uint32_t)) return DIT_ERR_WORKSPACE;
     dit::TailMerge tm;
-    memset(&tm, 0, sizeof(tm));
-    tm.pre_o = pre_o;
-    tm.pre_lse = pre_lse;
-    tm.claim = (uint32_t *)((char *)workspace + claim_off);
-    for (int i = 0; i < n_qb; ++i)
-      for (int p = 0; p < P; ++p)
-        if (!recompute[i * P + p]) tm.reuse_mask[i] |= (uint64_t)1 << p;
-    // chunks: about 8 per resident workgroup slot of the device, 1 to 16 passes each
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return DIT_ERR_HIP;
-    const int64_t slots = std::max<int64_t>(1, (int64_t)cus * dit::kMinBlocks);
-    const int64_t rpw = 256 / (D / 8);
-    const int64_t passes = ((int64_t)B * S_q * H + rpw - 1) / rpw;
-    const int64_t chunk_passes = std::min<int64_t>(16, std::max<int64_t>(1, passes / (8 * slots)));
-    const int64_t n_chunks = (passes + chunk_passes - 1) / chunk_passes;
-    const int64_t n_attn = (int64_t)B * H * desc.items_per_head;
-    const int64_t n_tail = std::min(n_chunks, slots);
-    // every tail workgroup ends with one failed claim: the counter reaches n_chunks + n_tail
-    if ((n_attn + n_tail) * (dit::kWaves * 64) > (int64_t)UINT32_MAX || n_chunks + n_tail > (int64_t)UINT32_MAX)
-      return DIT_ERR_SHAPE;
-    tm.n_attn_wg = (int32_t)n_attn;
-    tm.n_tail_wg = (int32_t)n_tail;
-    tm.n_chunks = (int32_t)n_chunks;
-    tm.chunk_passes = (int32_t)chunk_passes;
+    if ((st = make_tail(desc, recompute, B, S_q, H, D, n_qb, P, pre_o, pre_lse, workspace, tm))) return st;
     if (dit::launch_partition_attention_premerge(D, q, k, v, cache_o, cache_lse,
                                                  want_delta ? (float *)workspace : nullptr, desc,
                                                  scale_log2_of(softmax_scale, D), tm, as_stream(stream)) != hipSuccess)
