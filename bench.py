@@ -59,8 +59,8 @@ def kernel_source_sha256() -> str:
     return hashlib.sha256(b"".join(open(os.path.join(d, f), "rb").read() for f in ("kernels.hip", "launch.h"))).hexdigest()
 
 
-def measured_counters(workload: str) -> dict:
-    """Counter-derived figures of the attention kernel (clock under load, MFMA busy fraction)
+def measured_counters(workload: str, kernel: str) -> dict:
+    """Counter-derived figures of an attention launch (clock under load, MFMA busy fraction)
     from the committed rocprofv3 summary of this workload; empty when the kernel sources
     changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
@@ -69,7 +69,11 @@ def measured_counters(workload: str) -> dict:
     rec = json.load(open(path))
     if rec.get("source_sha256") != kernel_source_sha256():
         return {}
-    return rec.get("attention_counters", {})
+    for key in ("attention_counters", "plain_attention_counters"):
+        c = rec.get(key, {})
+        if c.get("kernel") == "dit::" + kernel:
+            return c
+    return {}
 
 
 def measured_power(workload: str) -> dict:
@@ -572,10 +576,23 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
         log(f"[bench] {w.name}: plain step {plain['ms_per_step']:.3f} ms  attention {plain['attention_ms']:.3f} ms "
             f"({plain['attention_tflops']:.1f} TFLOP/s)  merge in the step {plain['merge_in_step_ms']:.3f} ms")
     traffic = measured_traffic(w.name)
-    attn_counters = measured_counters(w.name)
-    if attn_counters and attn_counters.get("kernel") != "dit::" + attn_kernel:
-        attn_counters = {}
     merge_kernel = f"state_merge_kernel<128, {16 if w.P <= 16 else 32 if w.P <= 32 else 64}, false>"
+
+    def attn_roofline(kernel, ms):
+        tf = flop / (ms * 1e-3) / 1e12
+        c = measured_counters(w.name, kernel)
+        return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic.get("dit::" + kernel), "kernel": kernel,
+                "ms": round(ms, 4), "algorithmic_flop": flop, "counters": c or None,
+                "frac_of_clock_peak": round(tf / c["peak_tflops_at_that_clock"], 4) if c else None}
+
+    # roofline: the partition-attention kernel (a2) itself.  On a reuse step the step's launch
+    # also carries the pre-merge of the reused states: its figure is roofline_step_launch, and
+    # the attention kernel's own comes from the plain steps of the same run.
+    plain_kernel = "partition_attention_kernel<128, false>"
+    roof = attn_roofline(plain_kernel, plain["attention_ms"] if plain else attn_ms)
+    roof["timed_in"] = "the plain steps (attention launch, then the merge of all P states)" if plain else "the step"
+    roof["power"] = measured_power(w.name) or None
     res = {
         "ms_per_step": round(ms_step, 4),
         "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
@@ -584,14 +601,8 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
                    "recomputed_groups_per_block": w.recompute_groups,
                    "recomputed_pairs": int(mask.sum()), "reused_pairs": int(mask.size - mask.sum()),
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic.get("dit::" + attn_kernel),
-                     "kernel": attn_kernel, "ms": round(attn_ms, 4),
-                     "algorithmic_flop": flop, "counters": attn_counters or None,
-                     "frac_of_clock_peak": (round(attn_tflops / attn_counters["peak_tflops_at_that_clock"], 4)
-                                            if attn_counters else None),
-                     "power": measured_power(w.name) or None},
+        "roofline": roof,
+        "roofline_step_launch": attn_roofline(attn_kernel, attn_ms) if pre else None,
         "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
                            "traffic": traffic.get("dit::" + merge_kernel),

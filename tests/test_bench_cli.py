@@ -33,10 +33,12 @@ def test_counter_record_follows_the_same_source_hash():
     sys.path.insert(0, ROOT)
     import bench
     rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_video720p.json")))
-    got = bench.measured_counters("video720p")
-    if rec["source_sha256"] != bench.kernel_source_sha256():
-        assert got == {}
-        return
-    assert 0.5 < got["clock_ghz_under_load"] <= 2.4
-    assert 0.0 < got["mfma_busy_frac"] <= 1.0
-    assert abs(got["peak_tflops_at_that_clock"] - 2500.0 * got["clock_ghz_under_load"] / 2.4) < 1.0
+    for kernel in ("partition_attention_kernel<128, false>", "partition_attention_premerge_kernel<128>"):
+        got = bench.measured_counters("video720p", kernel)
+        if rec["source_sha256"] != bench.kernel_source_sha256():
+            assert got == {}
+            continue
+        assert got["kernel"] == "dit::" + kernel
+        assert 0.5 < got["clock_ghz_under_load"] <= 2.4
+        assert 0.0 < got["mfma_busy_frac"] <= 1.0
+        assert abs(got["peak_tflops_at_that_clock"] - 2500.0 * got["clock_ghz_under_load"] / 2.4) < 1.0
