@@ -491,29 +491,28 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
     valid = np.ones((w.n_qb, w.P), np.uint8)
 
     def one_step(t, events=None, plain=False):
-        """One step as dit_attn_partitioned runs it: on a step that reuses states, the reused
-        states are merged inside the attention launch into out / lse and a masked merge combines
-        the fresh states with them in place; otherwise (or with plain) the attention launch and
-        then the merge of all P states."""
+        """One step.  By default the library's one call (dit_attn_partitioned with the local
+        change): on a step that reuses states it merges them inside the attention launch and
+        finishes with the final combine.  With plain: the split calls of the plain sequence (the
+        attention kernel, the merge of all P states, the local-change finish), each between
+        events."""
         mask, _ = planner.next(t)
-        pre = not plain and not mask.all()
+        pre = not mask.all()
         if events:
             events[0].record(stream)
-        if pre:
-            api.partition_attention_premerge(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
-                                             sa.out, sa.lse, workspace=sa.workspace, local_part=w.local_part,
-                                             cache_valid=valid, stream=stream)
-        else:
-            api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
-                                    local_part=w.local_part, cache_valid=valid, workspace=sa.workspace,
-                                    stream=stream)
+        if not plain:
+            api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse, sa.out, sa.lse,
+                                 local_part=w.local_part, cache_valid=valid, delta_out=sa.delta,
+                                 workspace=sa.workspace, stream=stream)
+            if events:
+                for e in events[1:]:
+                    e.record(stream)
+            return mask, pre
+        api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
+                                local_part=w.local_part, cache_valid=valid, workspace=sa.workspace, stream=stream)
         if events:
             events[1].record(stream)
-        if pre:
-            api.state_merge_masked(sa.cache_o, sa.cache_lse, w.q_offsets, mask, sa.out, sa.lse, extra_o=sa.out,
-                                   extra_lse=sa.lse, stream=stream)
-        else:
-            api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
+        api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
         if events:
             events[2].record(stream)
         api.local_change_finalize(sa.workspace, 1, w.S_q, w.H, w.D, w.q_offsets, sa.delta, stream=stream)
@@ -534,20 +533,20 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
                 float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
                 float(np.mean([e[2].elapsed_time(e[3]) for e in ev])))
 
-    mask, pre, ms_step, attn_ms, merge_in_step_ms, fin_ms = timed(False)
+    # the step as the library runs it (device time of the one call between events), then the
+    # plain sequence with an event between its kernels (the attention kernel's roofline)
+    mask, pre, ms_step, step_dev_ms, _, _ = timed(False)
     # the GPU's output of the step, for the parity check beside the oracle
     rows = np.arange(w.S_q) if w.S_q <= 4096 else W.sample_rows(w, tiles_per_block=2, tile=128)
     ridx = torch.as_tensor(rows, device=dev)
     gpu_out = W.to_f64(sa.out[0, ridx].view(torch.int16).cpu().numpy().view(np.uint16))
     gpu_lse = sa.lse[0][:, ridx].double().cpu().numpy()
     # the same steps with the plain sequence (attention launch, then the merge of all P states)
-    plain = None
-    if pre:
-        _, _, p_ms, p_attn_ms, p_merge_ms, _ = timed(True)
-        p_out = W.to_f64(sa.out[0, ridx].view(torch.int16).cpu().numpy().view(np.uint16))
-        plain = {"ms_per_step": round(p_ms, 4), "attention_ms": round(p_attn_ms, 4),
-                 "merge_in_step_ms": round(p_merge_ms, 4), "kernel": "partition_attention_kernel<128, false>",
-                 "max_abs_diff_vs_step_out": float(np.abs(p_out - gpu_out).max())}
+    _, _, p_ms, attn_ms, merge_in_step_ms, fin_ms = timed(True)
+    p_out = W.to_f64(sa.out[0, ridx].view(torch.int16).cpu().numpy().view(np.uint16))
+    plain = {"ms_per_step": round(p_ms, 4), "attention_ms": round(attn_ms, 4),
+             "merge_in_step_ms": round(merge_in_step_ms, 4), "kernel": "partition_attention_kernel<128, false>",
+             "max_abs_diff_vs_step_out": float(np.abs(p_out - gpu_out).max())}
 
     # the merge alone on a cold cache (rotating over copies of the cache); the importance
     # variant of anchor steps on the same copies
@@ -564,51 +563,44 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
     mbytes = merge_bytes(w)
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
     merge_gbs = mbytes / (merge_ms * 1e-3) / 1e9
-    attn_kernel = "partition_attention_premerge_kernel<128>" if pre else "partition_attention_kernel<128, false>"
-    log(f"[bench] {w.name}: step {ms_step:.3f} ms  attention launch {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s"
-        f"{', with the reuse pre-merge' if pre else ''})  {'final combine' if pre else 'merge'} in the step "
-        f"{merge_in_step_ms:.3f} ms  merge of all planes {merge_ms:.3f} ms cold ({merge_gbs:.0f} GB/s; with importance "
-        f"{anchor_merge_ms:.3f} ms)  finalize {fin_ms:.4f} ms")
-    if plain:
-        plain["value"] = round(flop / (plain["ms_per_step"] * 1e-3) / 1e12, 2)
-        plain["attention_tflops"] = round(flop / (plain["attention_ms"] * 1e-3) / 1e12, 2)
-        plain["attention_frac"] = round(plain["attention_tflops"] / PEAK_BF16_TFLOPS, 4)
-        log(f"[bench] {w.name}: plain step {plain['ms_per_step']:.3f} ms  attention {plain['attention_ms']:.3f} ms "
-            f"({plain['attention_tflops']:.1f} TFLOP/s)  merge in the step {plain['merge_in_step_ms']:.3f} ms")
+    plain["value"] = round(flop / (plain["ms_per_step"] * 1e-3) / 1e12, 2)
+    how = ", the reused states merged in the attention launch" if pre else ""
+    log(f"[bench] {w.name}: step {ms_step:.3f} ms (device {step_dev_ms:.3f} ms{how})  plain step "
+        f"{plain['ms_per_step']:.3f} ms: attention {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s), merge "
+        f"{merge_in_step_ms:.3f} ms, finalize {fin_ms:.4f} ms  merge cold {merge_ms:.3f} ms ({merge_gbs:.0f} GB/s; "
+        f"with importance {anchor_merge_ms:.3f} ms)")
     traffic = measured_traffic(w.name)
     merge_kernel = f"state_merge_kernel<128, {16 if w.P <= 16 else 32 if w.P <= 32 else 64}, false>"
-
-    def attn_roofline(kernel, ms):
-        tf = flop / (ms * 1e-3) / 1e12
-        c = measured_counters(w.name, kernel)
-        return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic.get("dit::" + kernel), "kernel": kernel,
-                "ms": round(ms, 4), "algorithmic_flop": flop, "counters": c or None,
-                "frac_of_clock_peak": round(tf / c["peak_tflops_at_that_clock"], 4) if c else None}
-
-    # roofline: the partition-attention kernel (a2) itself.  On a reuse step the step's launch
-    # also carries the pre-merge of the reused states: its figure is roofline_step_launch, and
-    # the attention kernel's own comes from the plain steps of the same run.
+    # roofline: the partition-attention kernel (a2) itself, from the plain steps of the same run
+    # (on a reuse step the step's own launch also carries the pre-merge of the reused states)
     plain_kernel = "partition_attention_kernel<128, false>"
-    roof = attn_roofline(plain_kernel, plain["attention_ms"] if plain else attn_ms)
-    roof["timed_in"] = "the plain steps (attention launch, then the merge of all P states)" if plain else "the step"
-    roof["power"] = measured_power(w.name) or None
+    counters = measured_counters(w.name, plain_kernel)
+    roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic.get("dit::" + plain_kernel),
+            "kernel": plain_kernel, "ms": round(attn_ms, 4), "algorithmic_flop": flop,
+            "timed_in": "the plain steps of the same run (attention kernel, merge of all P states, finish)",
+            "counters": counters or None,
+            "frac_of_clock_peak": (round(attn_tflops / counters["peak_tflops_at_that_clock"], 4)
+                                   if counters else None),
+            "power": measured_power(w.name) or None}
     res = {
         "ms_per_step": round(ms_step, 4),
         "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "step_device_ms": round(step_dev_ms, 4),
+        "step": ("dit_attn_partitioned: the reused states merged inside the attention launch, then the final "
+                 "combine, then the local-change finish" if pre else
+                 "dit_attn_partitioned: attention launch, merge of all states, local-change finish"),
         "config": {"workload": w.name, "tokens": w.S_kv, "query_tokens": w.S_q, "heads": w.H, "head_dim": w.D,
                    "partitions": w.P, "query_blocks": w.n_qb, "group_size": int(np.diff(w.group_offsets)[0]),
                    "recomputed_groups_per_block": w.recompute_groups,
                    "recomputed_pairs": int(mask.sum()), "reused_pairs": int(mask.size - mask.sum()),
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "roofline_step_launch": attn_roofline(attn_kernel, attn_ms) if pre else None,
         "roofline_merge": {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
                            "traffic": traffic.get("dit::" + merge_kernel),
                            "kernel": merge_kernel, "ms": round(merge_ms, 4),
-                           "in_step": ("final combine (masked merge of the fresh planes and the pre-merged state)"
-                                       if pre else "this merge"), "ms_in_step": round(merge_in_step_ms, 4),
+                           "ms_in_plain_step": round(merge_in_step_ms, 4),
                            "algorithmic_bytes": mbytes,
                            "timing": "median over launches rotating over copies of the cache (cold MALL)",
                            "anchor_ms": round(anchor_merge_ms, 4),
@@ -616,7 +608,7 @@ def layer_bench(w: W.Workload, args, dev, extras: bool) -> dict:
         "local_change_finalize_ms": round(fin_ms, 5),
         "plain_step": plain,
     }
-    plain_ms = plain["ms_per_step"] if plain else ms_step
+    plain_ms = plain["ms_per_step"]
     ctx = {"X": X, "Xp": Xp, "mask": mask, "rows": rows, "gpu_out": gpu_out, "gpu_lse": gpu_lse,
            "q": q, "k": k, "v": v, "sa": sa, "planner": planner, "flop": flop, "ms_step": ms_step,
            "plain_ms_step": plain_ms, "merge_ms": merge_ms}
