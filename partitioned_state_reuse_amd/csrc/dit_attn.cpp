@@ -168,15 +168,13 @@ float scale_log2_of(float softmax_scale, int D) {
 
 // The reuse work of an attention launch (the merge of each block's reused planes into
 // pre_o / pre_lse by workgroups dispatched after the attention items): its description, with
-// its two counters at the start of the workspace's second region.  The workspace must hold
-// claim_offset(...) + kClaimBytes bytes.
+// the chunk counter at the start of the workspace's second region.  The workspace must hold
+// claim_offset(...) + 4 bytes.
 size_t claim_offset(int B, int S_q, int H, int n_qb) { return imp_ws_offset(B, S_q, H, n_qb); }
-constexpr size_t kClaimBytes = 2 * sizeof(uint32_t);
 
 int make_tail(const AttnDesc &desc, const uint8_t *recompute, int B, int S_q, int H, int D, int n_qb, int P,
-              void *pre_o, float *pre_lse, void *workspace, bool stop_early, dit::TailMerge &tm) {
+              void *pre_o, float *pre_lse, void *workspace, dit::TailMerge &tm) {
   memset(&tm, 0, sizeof(tm));
-  tm.stop_early = stop_early ? 1 : 0;
   tm.pre_o = pre_o;
   tm.pre_lse = pre_lse;
   tm.claim = (uint32_t *)((char *)workspace + claim_offset(B, S_q, H, n_qb));
@@ -230,15 +228,14 @@ int run_partitioned(const void *q, const void *k, const void *v, int B, int S_q,
     hipStream_t s = as_stream(stream);
     // A step that reuses some slot and asks for no importance (which the full merge computes)
     // takes the reused states' merge into the attention launch, into out / lse, when the
-    // workspace can hold the counters: its workgroups merge what they reach before the
-    // attention work ends, and the final combine merges the fresh states with that partial
-    // state in place (redoing the same arithmetic for the rows the launch did not reach).
+    // workspace can hold the chunk counter; a masked merge then combines the fresh states with
+    // that partial state in place.
     bool any_reuse = false;
     for (int e = 0; e < n_qb * P && !any_reuse; ++e) any_reuse = recompute[e] == 0;
     if (importance_out == nullptr && any_reuse && workspace != nullptr &&
-        workspace_bytes >= claim_offset(B, S_q, H, n_qb) + kClaimBytes) {
+        workspace_bytes >= claim_offset(B, S_q, H, n_qb) + sizeof(uint32_t)) {
       dit::TailMerge tm;
-      if ((st = make_tail(desc, recompute, B, S_q, H, D, n_qb, P, out, lse, workspace, true, tm))) return st;
+      if ((st = make_tail(desc, recompute, B, S_q, H, D, n_qb, P, out, lse, workspace, tm))) return st;
       if (dit::launch_partition_attention_premerge(D, q, k, v, cache_o, cache_lse,
                                                    want_delta ? (float *)workspace : nullptr, desc,
                                                    scale_log2_of(softmax_scale, D), tm, s) != hipSuccess)
@@ -251,7 +248,7 @@ int run_partitioned(const void *q, const void *k, const void *v, int B, int S_q,
       for (int i = 0; i < n_qb; ++i)
         for (int p = 0; p < P; ++p)
           if (recompute[i * P + p]) sel.plane_mask[i] |= (uint64_t)1 << p;
-      if (dit::launch_state_merge_tail_combine(D, P, cache_o, cache_lse, sel, tm, out, lse, B, S_q, H, s) !=
+      if (dit::launch_state_merge_masked(D, P, cache_o, cache_lse, out, lse, sel, out, lse, B, S_q, H, s) !=
           hipSuccess)
         return DIT_ERR_HIP;
     } else {
@@ -335,11 +332,11 @@ int dit_partition_attention_premerge(const void *q, const void *k, const void *v
     int st = build_attn(q, k, v, B, S_q, S_kv, H, D, q_offsets, n_qb, kv_offsets, P, local_part, recompute,
                         cache_valid, cache_o, cache_lse, want_delta, workspace, workspace_bytes, desc);
     if (st) return st;
-    // the counters sit at the start of the workspace's second region; every row is pre-merged
+    // the chunk counter sits at the start of the workspace's second region
     if (!workspace) return DIT_ERR_WORKSPACE;
-    if (workspace_bytes < claim_offset(B, S_q, H, n_qb) + kClaimBytes) return DIT_ERR_WORKSPACE;
+    if (workspace_bytes < claim_offset(B, S_q, H, n_qb) + sizeof(uint32_t)) return DIT_ERR_WORKSPACE;
     dit::TailMerge tm;
-    if ((st = make_tail(desc, recompute, B, S_q, H, D, n_qb, P, pre_o, pre_lse, workspace, false, tm))) return st;
+    if ((st = make_tail(desc, recompute, B, S_q, H, D, n_qb, P, pre_o, pre_lse, workspace, tm))) return st;
     if (dit::launch_partition_attention_premerge(D, q, k, v, cache_o, cache_lse,
                                                  want_delta ? (float *)workspace : nullptr, desc,
                                                  scale_log2_of(softmax_scale, D), tm, as_stream(stream)) != hipSuccess)

@@ -712,9 +712,9 @@ __device__ __forceinline__ void merge_rows(const MergeGrid &g, int w, int S_q, i
 // order); the weights w_p = e^{lse_p - lse} (times s_p) go to wts[0 .. PMAX) in LDS, where
 // every lane of the group reads them, and, when `wraw` is given, the weights without the
 // scale to wraw.  Planes at or past P, planes outside the mask `pm`, empty states and row-heads
-// that are not `valid` (no loads at all) get weight 0.  An extra state (has_x, its lse x_lse
-// as seen by lane 0 of the group) takes part in the merge with its weight in wts[PMAX].
-// Returns the merged lse (-inf when every state is empty).
+// that are not `valid` (no loads at all) get weight 0.  An extra state (extra_lse non-null,
+// its lse at index xi loaded by lane 0) takes part in the merge with its weight in
+// wts[PMAX].  Returns the merged lse (-inf when every state is empty).
 // Reduction over the TPR lanes of a row-head group (aligned runs of TPR lanes), every lane
 // ending with the result in a fixed order.  With kMergeDpp the lanes exchange values through
 // DPP moves inside rows of 16 lanes (quad swaps, then the half-row and row mirrors), else
@@ -741,8 +741,9 @@ template <int TPR, int PMAX, bool SCALED>
 __device__ __forceinline__ float group_merge_weights(const float *__restrict__ cache_lse,
                                                      const float *__restrict__ cache_scale, int64_t ci,
                                                      int64_t plane_lse, int P, int c, bool valid, float *wts,
-                                                     float *wraw, uint64_t pm = ~0ull, bool has_x = false,
-                                                     float x_lse = -INFINITY) {
+                                                     float *wraw, uint64_t pm = ~0ull,
+                                                     const float *__restrict__ extra_lse = nullptr,
+                                                     int64_t xi = 0) {
   constexpr int NPL = (PMAX + TPR - 1) / TPR;
   float lv[NPL];
   float M = -INFINITY;
@@ -752,7 +753,7 @@ __device__ __forceinline__ float group_merge_weights(const float *__restrict__ c
     lv[k] = (valid && p < P && ((pm >> p) & 1)) ? cache_lse[p * plane_lse + ci] : -INFINITY;
     M = fmaxf(M, lv[k]);
   }
-  const float lx = (valid && has_x && c == 0) ? x_lse : -INFINITY;
+  const float lx = (valid && extra_lse != nullptr && c == 0) ? extra_lse[xi] : -INFINITY;
   M = fmaxf(M, lx);
   M = group_reduce<TPR>(M, [](float a, float b) { return fmaxf(a, b); });
   float sum = (lx > -INFINITY) ? __expf(lx - M) : 0.f;
@@ -770,7 +771,7 @@ __device__ __forceinline__ float group_merge_weights(const float *__restrict__ c
       wts[p] = w;
     }
   }
-  if (has_x && c == 0) wts[PMAX] = (lx > -INFINITY) ? __expf(lx - L) : 0.f;
+  if (extra_lse != nullptr && c == 0) wts[PMAX] = (lx > -INFINITY) ? __expf(lx - L) : 0.f;
   // the group's lanes are in this wave: LDS accesses of one wave complete in order, and
   // the barrier keeps the compiler from moving the readers' loads above these stores
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -951,25 +952,37 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
 }
 
 // Masked merge of one row-head rh by its TPR lanes (this lane is number c of them): the
-// cache planes in pm, in increasing order, then, with has_x, an extra state whose lse is x_lse
-// (as seen by lane 0) and whose 8 bf16 values at this lane's d are x_o; the merged values in
-// fp32 go to acc.  wts: the group's PMAX + 1 weights in LDS.  Returns the merged lse.
-template <int D, int PMAX, int BATCH = kMaskedMergeBatch>
-__device__ __forceinline__ float masked_merge_core(const u16 *__restrict__ cache_o,
-                                                   const float *__restrict__ cache_lse, const int64_t rh,
-                                                   const uint64_t pm, const int P, const int64_t plane_o,
-                                                   const int64_t plane_lse, const int c, float *wts,
-                                                   const bool has_x, const float x_lse, const u32x4 x_o,
-                                                   float (&acc)[8]) {
+// cache planes in pm, in increasing order, plus the extra state when extra_lse is non-null
+// (a partial composition made earlier, its lse in the [B, H, S_q] layout of a merged output,
+// at index xi, which is also where the merged lse goes).  wts: the group's PMAX + 1 weights
+// in LDS.
+template <int D, int PMAX>
+__device__ __forceinline__ void masked_merge_rowhead(const u16 *__restrict__ cache_o,
+                                                     const float *__restrict__ cache_lse,
+                                                     const u16 *__restrict__ extra_o,
+                                                     const float *__restrict__ extra_lse, u16 *__restrict__ out,
+                                                     float *__restrict__ lse_out, const int64_t rh,
+                                                     const int64_t xi, const uint64_t pm, const int P,
+                                                     const int64_t plane_o, const int64_t plane_lse, const int c,
+                                                     float *wts) {
   constexpr int TPR = D / 8;
   const float L = group_merge_weights<TPR, PMAX, false>(cache_lse, nullptr, rh, plane_lse, P, c, true, wts, nullptr,
-                                                        pm, has_x, x_lse);
+                                                        pm, extra_lse, xi);
+  float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  auto add = [&](const u16 *src, float w) {
+    const u32x4 u = __builtin_nontemporal_load((const u32x4 *)src);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc[2 * t] += w * bf16_bits_to_f32(u[t] & 0xffffu);
+      acc[2 * t + 1] += w * bf16_bits_to_f32(u[t] >> 16);
+    }
+  };
   const u16 *src = cache_o + rh * D + 8 * c;
   // the selected planes in increasing order, NB loads in flight at a time; a short last
   // batch re-reads its first plane in place of the missing ones (never added)
-  constexpr int NB = PMAX < BATCH ? PMAX : BATCH;
+  constexpr int NB = PMAX < kMaskedMergeBatch ? PMAX : kMaskedMergeBatch;
   uint64_t rest = pm & (P < 64 ? ((uint64_t)1 << P) - 1 : ~(uint64_t)0);
   while (rest) {
     int pi[NB];
@@ -1000,40 +1013,13 @@ __device__ __forceinline__ float masked_merge_core(const u16 *__restrict__ cache
       }
     }
   }
-  if (has_x) {
-    const float w = wts[PMAX];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc[2 * t] += w * bf16_bits_to_f32(x_o[t] & 0xffffu);
-      acc[2 * t + 1] += w * bf16_bits_to_f32(x_o[t] >> 16);
-    }
-  }
-  return L;
-}
-
-__device__ __forceinline__ u32x4 pack_bf16x8(const float (&acc)[8]) {
-  return u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-               pack_bf16x2(acc[6], acc[7])};
-}
-
-// Masked merge of one row-head with the extra state in memory (extra_lse non-null: its lse at
-// index xi of the [B, H, S_q] layout of a merged output, which is also where the merged lse
-// goes); the result is written to out / lse_out.  The extra state may be out / lse_out
-// themselves: every lane reads its own extra values before it writes the same ones.
-template <int D, int PMAX, int BATCH = kMaskedMergeBatch>
-__device__ __forceinline__ void masked_merge_rowhead(const u16 *__restrict__ cache_o,
-                                                     const float *__restrict__ cache_lse, const u16 *extra_o,
-                                                     const float *extra_lse, u16 *out, float *lse_out,
-                                                     const int64_t rh, const int64_t xi, const uint64_t pm,
-                                                     const int P, const int64_t plane_o, const int64_t plane_lse,
-                                                     const int c, float *wts) {
-  const bool has_x = extra_lse != nullptr;
-  const float x_lse = (has_x && c == 0) ? extra_lse[xi] : -INFINITY;
-  const u32x4 x_o = has_x ? __builtin_nontemporal_load((const u32x4 *)(extra_o + rh * D + 8 * c)) : u32x4{0u, 0u, 0u, 0u};
-  float acc[8];
-  const float L = masked_merge_core<D, PMAX, BATCH>(cache_o, cache_lse, rh, pm, P, plane_o, plane_lse, c, wts, has_x,
-                                                    x_lse, x_o, acc);
-  __builtin_nontemporal_store(pack_bf16x8(acc), (u32x4 *)(out + rh * D + 8 * c));
+  if (extra_lse != nullptr) add(extra_o + rh * D + 8 * c, wts[PMAX]);
+  uint4 res;
+  res.x = pack_bf16x2(acc[0], acc[1]);
+  res.y = pack_bf16x2(acc[2], acc[3]);
+  res.z = pack_bf16x2(acc[4], acc[5]);
+  res.w = pack_bf16x2(acc[6], acc[7]);
+  __builtin_nontemporal_store(u32x4{res.x, res.y, res.z, res.w}, (u32x4 *)(out + rh * D + 8 * c));
   if (c == 0) lse_out[xi] = L;
 }
 
@@ -1082,10 +1068,7 @@ __global__ __launch_bounds__(256) void state_merge_masked_kernel(
 // launch) until none is left, and merges, for every row-head of a chunk, the cache planes
 // its query block reuses (tm.reuse_mask) into the partial state pre_o / pre_lse: the
 // masked merge, on planes that this launch does not write.  Chunks are claimed in order, so
-// the XCDs that run out of attention items first take more of them.  With tm.stop_early the
-// workgroups stop claiming once every attention workgroup has finished (the counter
-// tm.claim[1] counts them): the claimed chunks are then [0, min(tm.claim[0], n_chunks)), and
-// state_merge_tail_combine_kernel does the rest at the merge's own occupancy.
+// the XCDs that run out of attention items first take more of them.
 // ------------------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void premerge_chunks(const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse,
@@ -1103,13 +1086,7 @@ __device__ __forceinline__ void premerge_chunks(const u16 *__restrict__ cache_o,
   float *wts = wts_all[threadIdx.x / TPR];
   u16 *pre_o = (u16 *)tm.pre_o;
   for (;;) {
-    if (threadIdx.x == 0) {
-      uint32_t got = UINT32_MAX;
-      if (!tm.stop_early ||
-          __hip_atomic_load(tm.claim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)tm.n_attn_wg)
-        got = __hip_atomic_fetch_add(tm.claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      claimed = got;
-    }
+    if (threadIdx.x == 0) claimed = __hip_atomic_fetch_add(tm.claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const uint32_t ch = claimed;
     __syncthreads();  // every thread has read it before the next claim overwrites it
@@ -1140,55 +1117,10 @@ __global__ __launch_bounds__(kWaves * 64, kMinBlocks) void partition_attention_p
   }
   attention_item<D, false>(q, k, v, cache_o, nullptr, cache_lse, delta_part, desc, scale_log2, tm.n_attn_wg,
                            blockIdx.x);
-  // count the finished attention workgroups (only what the pre-merge workgroups look at)
-  if (tm.stop_early && threadIdx.x == 0)
-    __hip_atomic_fetch_add(tm.claim + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The chunk counter and the finished-workgroup counter of a launch with the pre-merge.
 __global__ void clear_claim_kernel(uint32_t *claim) {
-  if (threadIdx.x < 2) claim[threadIdx.x] = 0u;
-}
-
-// The final combine of a step whose reused states were pre-merged in the attention launch
-// with tm.stop_early: row-heads of the claimed chunks combine their block's fresh planes
-// (sel.plane_mask) with the partial state in out / lse, in place; the others first redo the
-// pre-merge's arithmetic in registers (the merge of the reused planes, rounded to bf16 as
-// the pre-merge stores it), then combine the same way.  So the result does not depend on
-// how far the pre-merge got before the attention work ended.
-template <int D, int PMAX>
-__global__ __launch_bounds__(256) void state_merge_tail_combine_kernel(
-    const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, const MergeSelect sel,
-    const uint32_t *__restrict__ claim, const int n_chunks, const int64_t chunk_rh, u16 *out, float *lse_out,
-    const int S_q, const int H, const int P, const int64_t total_rh, const int64_t plane_o, const int64_t plane_lse,
-    const int chunk) {
-  constexpr int TPR = D / 8;
-  constexpr int RPW = 256 / TPR;
-  const int64_t rh = (int64_t)lse_chunked_item(chunk) * RPW + threadIdx.x / TPR;
-  if (rh >= total_rh) return;
-  const int c = threadIdx.x % TPR;
-  const int64_t br = rh / H;
-  const int h = (int)(rh - br * H);
-  const int64_t b = br / S_q;
-  const int r = (int)(br - b * S_q);
-  const int64_t xi = (b * H + h) * S_q + r;
-  const uint64_t fresh = sel.plane_mask[block_of_row(sel.q_off, sel.n_qb, r)];
-  const uint64_t reused = (P < 64 ? ((uint64_t)1 << P) - 1 : ~(uint64_t)0) & ~fresh;
-  const uint32_t n_claimed = min(*claim, (uint32_t)n_chunks);
-  __shared__ float wts_all[RPW][PMAX + 1];
-  float *wts = wts_all[threadIdx.x / TPR];
-  if ((uint64_t)(rh / chunk_rh) < n_claimed) {
-    masked_merge_rowhead<D, PMAX>(cache_o, cache_lse, out, lse_out, out, lse_out, rh, xi, fresh, P, plane_o, plane_lse,
-                                  c, wts);
-    return;
-  }
-  float part[8], acc[8];
-  const float L1 = masked_merge_core<D, PMAX>(cache_o, cache_lse, rh, reused, P, plane_o, plane_lse, c, wts, false,
-                                              -INFINITY, u32x4{0u, 0u, 0u, 0u}, part);
-  const float L = masked_merge_core<D, PMAX>(cache_o, cache_lse, rh, fresh, P, plane_o, plane_lse, c, wts, true, L1,
-                                             pack_bf16x8(part), acc);
-  __builtin_nontemporal_store(pack_bf16x8(acc), (u32x4 *)(out + rh * D + 8 * c));
-  if (c == 0) lse_out[xi] = L;
+  if (threadIdx.x == 0) *claim = 0u;
 }
 
 template <int D>
@@ -1449,37 +1381,6 @@ hipError_t launch_partition_attention_premerge(int D, const void *q, const void 
   else
     hipLaunchKernelGGL((partition_attention_premerge_kernel<64>), grid, block, 0, stream, qq, kk, vv, cache_o,
                        cache_lse, delta_partials, desc, scale_log2, tm);
-  return hipGetLastError();
-}
-
-hipError_t launch_state_merge_tail_combine(int D, int P, const void *cache_o, const float *cache_lse,
-                                           const MergeSelect &sel, const TailMerge &tm, void *out, float *lse, int B,
-                                           int S_q, int H, hipStream_t stream) {
-  (void)hipGetLastError();
-  const int64_t total_rh = (int64_t)B * S_q * H;
-  if (total_rh == 0) return hipSuccess;
-  const int rpw = 256 / (D / 8);
-  const int64_t nwg = (total_rh + rpw - 1) / rpw;
-  const int64_t plane_o = total_rh * D;
-  const int chunk = merge_chunk(rpw, H);
-  const int64_t chunk_rh = (int64_t)tm.chunk_passes * rpw;
-  dim3 grid((unsigned)nwg), block(256);
-  const u16 *co = (const u16 *)cache_o;
-  u16 *oo = (u16 *)out;
-#define DIT_TAIL_COMBINE(DD, PM)                                                                                  \
-  hipLaunchKernelGGL((state_merge_tail_combine_kernel<DD, PM>), grid, block, 0, stream, co, cache_lse, sel,      \
-                     (const uint32_t *)tm.claim, tm.n_chunks, chunk_rh, oo, lse, S_q, H, P, total_rh, plane_o,   \
-                     total_rh, chunk)
-  if (D == 128) {
-    if (P <= 16) DIT_TAIL_COMBINE(128, 16);
-    else if (P <= 32) DIT_TAIL_COMBINE(128, 32);
-    else DIT_TAIL_COMBINE(128, 64);
-  } else {
-    if (P <= 16) DIT_TAIL_COMBINE(64, 16);
-    else if (P <= 32) DIT_TAIL_COMBINE(64, 32);
-    else DIT_TAIL_COMBINE(64, 64);
-  }
-#undef DIT_TAIL_COMBINE
   return hipGetLastError();
 }
 

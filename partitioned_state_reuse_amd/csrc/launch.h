@@ -100,26 +100,22 @@ hipError_t launch_partition_attention(int D, bool fp8_cache, const void *q, cons
 // after the n_attn_wg attention ones merge, for every query row, the cache planes its block
 // reuses (bit p of reuse_mask[i]: block i reuses plane p) into the partial state pre_o
 // [B, S_q, H, D] bf16, pre_lse [B, H, S_q] f32, claiming chunks of chunk_passes * 256 / (D / 8)
-// row-heads (n_chunks of them cover B * S_q * H) from the counter claim[0], which the launch
-// clears first.  stop_early: the workgroups stop claiming once all attention workgroups have
-// finished (counted in claim[1]); the rows left over are merged by
-// launch_state_merge_tail_combine.
+// row-heads (n_chunks of them cover B * S_q * H) from the counter `claim`, which the launch
+// clears first.
 struct TailMerge {
   void *pre_o;
   float *pre_lse;
-  uint32_t *claim;   // two counters
+  uint32_t *claim;
   int32_t n_attn_wg;
   int32_t n_tail_wg;
   int32_t n_chunks;
   int32_t chunk_passes;
-  int32_t stop_early;
   uint64_t reuse_mask[DIT_MAX_BLOCKS];
 };
 
 hipError_t launch_partition_attention_premerge(int D, const void *q, const void *k, const void *v, void *cache_o,
                                                float *cache_lse, float *delta_partials, const AttnDesc &desc,
                                                float scale_log2, const TailMerge &tm, hipStream_t stream);
-
 
 // Merges.  The cache's lse (and scale) planes are [P, B, S_q, H]; the merged lse goes out as
 // [B, H, S_q], or, with lse_rowmajor, as [B, S_q, H] (a cache plane: compose).  With
@@ -143,13 +139,6 @@ struct MergeSelect {
 hipError_t launch_state_merge_masked(int D, int P, const void *cache_o, const float *cache_lse,
                                      const void *extra_o, const float *extra_lse, const MergeSelect &sel,
                                      void *out, float *lse, int B, int S_q, int H, hipStream_t stream);
-
-// The final combine after a launch with the pre-merge and stop_early: rows of claimed chunks
-// merge their block's fresh planes (sel.plane_mask) with the partial state in out / lse;
-// the others redo the pre-merge's arithmetic first; the result is written to out / lse.
-hipError_t launch_state_merge_tail_combine(int D, int P, const void *cache_o, const float *cache_lse,
-                                           const MergeSelect &sel, const TailMerge &tm, void *out, float *lse, int B,
-                                           int S_q, int H, hipStream_t stream);
 
 hipError_t launch_state_merge(int D, int P, const void *cache_o, const float *cache_lse,
                               void *out, float *lse, int B, int S_q, int H, bool lse_rowmajor,
