@@ -199,7 +199,7 @@ def test_premerged_step_maximum_blocks_and_partitions(D):
 
 
 def _claimed_chunks(ws, w, B=1):
-    """Chunks the attention launch's pre-merge reached (its counter in the workspace: after
+    """Chunks the attention launch's pre-merge claimed (its counter in the workspace: after
     the local-change partials, from the next 256-byte boundary) and the chunk count."""
     delta = B * ((w.S_q + 127) // 128 + w.n_qb) * w.H * 8
     off = (delta + 255) // 256 * 256
@@ -213,9 +213,9 @@ def _claimed_chunks(ws, w, B=1):
 
 
 def _one_call_vs_split(w, mask):
-    """The one-call step (its launch's pre-merge stops when the attention work ends; the final
-    combine redoes the pre-merge's arithmetic for the rows it did not reach) against the split
-    sequence with the full pre-merge: bitwise equal outputs, cache and local change."""
+    """The one-call step (the pre-merge into out / lse inside the attention launch, then the
+    final combine in place) against the split sequence with a separate partial state: bitwise
+    equal outputs, cache and local change."""
     ones = np.ones((w.n_qb, w.P), np.uint8)
     Xp, X = W.make_step(w, -1), W.make_step(w, 0)
     base = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part)
@@ -244,6 +244,7 @@ def _one_call_vs_split(w, mask):
     a, b, c = runs["one_call"], runs["split"], runs["no_workspace"]
     got, n = _claimed_chunks(a[5], w)
     _log(w.name, f"one-call step: the attention launch pre-merged {got} of {n} chunks")
+    assert got == n
     for x, y, what in zip(a, b, ("out", "lse", "delta", "cache_o", "cache_lse")):
         assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y), what
@@ -268,113 +269,7 @@ def test_one_call_step_takes_the_premerge_in_place():
 
 @pytest.mark.parametrize("name", ["share32", "video720p"])
 def test_one_call_step_at_full_size_matches_the_split_sequence(name):
-    """Full size, where the launch's pre-merge reaches part of the rows (32-way share) or
-    nearly all (720p) before the attention work ends: still bitwise the split sequence."""
+    """Full size, in the benchmark's launch configuration: bitwise the split sequence."""
     w = W.workload(name)
     mask = np.asarray(PT.masks_from_planners(w)[0], np.uint8)
     _one_call_vs_split(w, mask)
-
-
-@pytest.mark.parametrize("D", [64, 128])
-def test_premerged_step_maximum_blocks_and_partitions(D):
-    """64 query blocks and 64 partitions (the largest counts; every plane bit in use)."""
-    from test_gpu_parity import _max_layout
-    w, qo, ko, local, mask = _max_layout(D, seed=93 + D)
-    _check_premerged_step(w, mask, np.arange(qo[-1]), qo=qo, ko=ko, local=local)
-
-
-def _claimed_chunks(ws, w, B=1):
-    """Chunks the attention launch's pre-merge reached (its counter in the workspace: after
-    the local-change partials, from the next 256-byte boundary) and the chunk count."""
-    delta = B * ((w.S_q + 127) // 128 + w.n_qb) * w.H * 8
-    off = (delta + 255) // 256 * 256
-    claimed = int(ws.view(torch.int32)[off // 4].item())
-    rpw = 256 // (w.D // 8)
-    passes = (B * w.S_q * w.H + rpw - 1) // rpw
-    slots = 3 * torch.cuda.get_device_properties(0).multi_processor_count
-    cp = min(16, max(1, passes // (8 * slots)))
-    n_chunks = (passes + cp - 1) // cp
-    return min(claimed, n_chunks), n_chunks
-
-
-def _one_call_vs_split(w, mask):
-    """The one-call step (its launch's pre-merge stops when the attention work ends; the final
-    combine redoes the pre-merge's arithmetic for the rows it did not reach) against the split
-    sequence with the full pre-merge: bitwise equal outputs, cache and local change."""
-    ones = np.ones((w.n_qb, w.P), np.uint8)
-    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
-    base = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part)
-    base.step(PT.to_dev(Xp.q), PT.to_dev(Xp.k), PT.to_dev(Xp.v), ones)
-    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
-    runs = {}
-    for name in ("one_call", "split", "no_workspace"):
-        co, cl = base.cache_o.clone(), base.cache_lse.clone()
-        out, lse = torch.full_like(base.out, float("nan")), torch.full_like(base.lse, float("nan"))
-        dl = torch.full_like(base.delta, float("nan"))
-        ws = torch.full_like(base.workspace, float("nan"))
-        if name == "one_call":
-            api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, mask, co, cl, out, lse, local_part=w.local_part,
-                                 cache_valid=ones, delta_out=dl, workspace=ws)
-        elif name == "split":
-            pre_o, pre_lse = torch.empty_like(base.out), torch.empty_like(base.lse)
-            api.partition_attention_premerge(q, k, v, w.q_offsets, w.kv_offsets, mask, co, cl, pre_o, pre_lse,
-                                             workspace=ws, local_part=w.local_part, cache_valid=ones)
-            api.state_merge_masked(co, cl, w.q_offsets, mask, out, lse, extra_o=pre_o, extra_lse=pre_lse)
-            api.local_change_finalize(ws, 1, w.S_q, w.H, w.D, w.q_offsets, dl)
-        else:
-            api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, mask, co, cl, out, lse, local_part=w.local_part,
-                                 cache_valid=ones)
-        torch.cuda.synchronize()
-        runs[name] = (out, lse, dl, co, cl, ws)
-    a, b, c = runs["one_call"], runs["split"], runs["no_workspace"]
-    got, n = _claimed_chunks(a[5], w)
-    _log(w.name, f"one-call step: the attention launch pre-merged {got} of {n} chunks")
-    for x, y, what in zip(a, b, ("out", "lse", "delta", "cache_o", "cache_lse")):
-        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
-                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y), what
-    assert torch.equal(a[3], c[3]) and torch.equal(a[4], c[4])
-    return a, c
-
-
-def test_one_call_step_takes_the_premerge_in_place():
-    """dit_attn_partitioned on a reuse step without importance: the reused states are merged
-    inside the attention launch into out / lse, then combined in place with the fresh ones.
-    Its outputs, cache and local change equal bitwise those of the split sequence with a
-    separate partial state (dit_partition_attention_premerge, dit_state_merge_masked,
-    dit_local_change_finalize); without a workspace the one-call step merges after the
-    attention launch, with the same result up to fp32 rounding order."""
-    w = W.workload("video720p", grid=(5, 18, 32), H=4)
-    mask = np.asarray(PT.masks_from_planners(w)[0], np.uint8)
-    ones = np.ones((w.n_qb, w.P), np.uint8)
-    Xp, X = W.make_step(w, -1), W.make_step(w, 0)
-    base = api.SelectiveAttention(1, w.S_q, w.S_kv, w.H, w.D, w.q_offsets, w.kv_offsets, w.local_part)
-    base.step(PT.to_dev(Xp.q), PT.to_dev(Xp.k), PT.to_dev(Xp.v), ones)
-    q, k, v = PT.to_dev(X.q), PT.to_dev(X.k), PT.to_dev(X.v)
-    runs = {}
-    for name in ("one_call", "split", "no_workspace"):
-        co, cl = base.cache_o.clone(), base.cache_lse.clone()
-        out, lse = torch.full_like(base.out, float("nan")), torch.full_like(base.lse, float("nan"))
-        dl = torch.full_like(base.delta, float("nan"))
-        ws = torch.full_like(base.workspace, float("nan"))
-        if name == "one_call":
-            api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, mask, co, cl, out, lse, local_part=w.local_part,
-                                 cache_valid=ones, delta_out=dl, workspace=ws)
-        elif name == "split":
-            pre_o, pre_lse = torch.empty_like(base.out), torch.empty_like(base.lse)
-            api.partition_attention_premerge(q, k, v, w.q_offsets, w.kv_offsets, mask, co, cl, pre_o, pre_lse,
-                                             workspace=ws, local_part=w.local_part, cache_valid=ones)
-            api.state_merge_masked(co, cl, w.q_offsets, mask, out, lse, extra_o=pre_o, extra_lse=pre_lse)
-            api.local_change_finalize(ws, 1, w.S_q, w.H, w.D, w.q_offsets, dl)
-        else:
-            api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, mask, co, cl, out, lse, local_part=w.local_part,
-                                 cache_valid=ones)
-        torch.cuda.synchronize()
-        runs[name] = (out, lse, dl, co, cl)
-    a, b, c = runs["one_call"], runs["split"], runs["no_workspace"]
-    for x, y, what in zip(a, b, ("out", "lse", "delta", "cache_o", "cache_lse")):
-        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
-                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y), what
-    assert torch.equal(a[3], c[3]) and torch.equal(a[4], c[4])
-    # the partial state is rounded to bf16 before the final combine: a row-scaled bound
-    PT.assert_rows_close(PT.bf16_to_f64(a[0][0]), PT.bf16_to_f64(c[0][0]), "one call with and without the pre-merge")
-    assert (a[1] - c[1]).abs().max().item() <= 1e-5
