@@ -742,8 +742,7 @@ __device__ __forceinline__ float group_merge_weights(const float *__restrict__ c
                                                      const float *__restrict__ cache_scale, int64_t ci,
                                                      int64_t plane_lse, int P, int c, bool valid, float *wts,
                                                      float *wraw, uint64_t pm = ~0ull,
-                                                     const float *__restrict__ extra_lse = nullptr,
-                                                     int64_t xi = 0) {
+                                                     const float *extra_lse = nullptr, int64_t xi = 0) {
   constexpr int NPL = (PMAX + TPR - 1) / TPR;
   float lv[NPL];
   float M = -INFINITY;
@@ -955,13 +954,13 @@ __global__ __launch_bounds__(256) void state_merge_fp8_kernel(
 // cache planes in pm, in increasing order, plus the extra state when extra_lse is non-null
 // (a partial composition made earlier, its lse in the [B, H, S_q] layout of a merged output,
 // at index xi, which is also where the merged lse goes).  wts: the group's PMAX + 1 weights
-// in LDS.
+// in LDS.  out / lse_out may be the extra state itself (every lane reads the extra values it
+// then overwrites, and no others), so those four pointers are not restrict-qualified.
 template <int D, int PMAX>
 __device__ __forceinline__ void masked_merge_rowhead(const u16 *__restrict__ cache_o,
                                                      const float *__restrict__ cache_lse,
-                                                     const u16 *__restrict__ extra_o,
-                                                     const float *__restrict__ extra_lse, u16 *__restrict__ out,
-                                                     float *__restrict__ lse_out, const int64_t rh,
+                                                     const u16 *extra_o, const float *extra_lse, u16 *out,
+                                                     float *lse_out, const int64_t rh,
                                                      const int64_t xi, const uint64_t pm, const int P,
                                                      const int64_t plane_o, const int64_t plane_lse, const int c,
                                                      float *wts) {
@@ -1040,9 +1039,9 @@ __device__ __forceinline__ int block_of_row(const int32_t *q_off, int n_qb, int 
 // recomputes the others, and to finish with the fresh states and that partial.
 template <int D, int PMAX>
 __global__ __launch_bounds__(256) void state_merge_masked_kernel(
-    const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, const u16 *__restrict__ extra_o,
-    const float *__restrict__ extra_lse, const MergeSelect sel, u16 *__restrict__ out,
-    float *__restrict__ lse_out, const int S_q, const int H, const int P, const int64_t total_rh,
+    const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse, const u16 *extra_o,
+    const float *extra_lse, const MergeSelect sel, u16 *out, float *lse_out, const int S_q, const int H,
+    const int P, const int64_t total_rh,
     const int64_t plane_o, const int64_t plane_lse, const int chunk) {
   constexpr int TPR = D / 8;
   constexpr int RPW = 256 / TPR;
