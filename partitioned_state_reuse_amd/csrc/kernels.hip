@@ -182,8 +182,17 @@ __device__ __forceinline__ void attention_item(
   const int H = desc.H;
   const int b = bh / H;
   const int head = bh - b * H;
+  // partition of the item: the last p < P with item_prefix[p] <= idx (a partition without
+  // items has the same prefix as the next one, so that p is the one that holds idx); a
+  // binary search keeps the chain of dependent scalar loads short when P is large
   int p = 0;
-  while (desc.item_prefix[p + 1] <= idx) ++p;
+  {
+    int hi = desc.P - 1;
+    while (p < hi) {
+      const int mid = (p + hi + 1) >> 1;
+      if (desc.item_prefix[mid] <= idx) p = mid; else hi = mid - 1;
+    }
+  }
   idx -= desc.item_prefix[p];
   uint64_t bm = desc.blocks_of_part[p];
   int blk = 0;
