@@ -90,8 +90,10 @@ const char *dit_status_string(int status);
 
 /* Bytes of device workspace dit_attn_partitioned needs for these sizes, for any split into
  * n_qb query blocks: the local-change partial sums of the attention kernel, then the
- * importance partials of the merge (P floats per merge workgroup).  The split calls take the
- * same workspace.  Returns 0 if the sizes are invalid. */
+ * importance partials of the merge (P floats per merge workgroup); a reuse step without
+ * importance keeps the in-launch pre-merge's chunk counter where the importance partials
+ * would go.  The split calls take the same workspace.  Calls in flight at the same time (on
+ * different streams) must not share a workspace.  Returns 0 if the sizes are invalid. */
 size_t dit_attn_workspace_bytes(int B, int S_q, int H, int D, int n_qb, int P);
 
 /*
