@@ -854,8 +854,10 @@ def main() -> int:
         return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 10; 100 for the short share32 and image_anchor steps)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default 2; 20 for share32 and image_anchor)")
     ap.add_argument("--workload", default="video720p", choices=["video720p", "share32", "image_anchor", "longvideo"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-share32", action="store_true", help="with the 720p layer: skip the 32-way-share object")
@@ -872,6 +874,13 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     w = W.workload(args.workload)
+    # a step of the short layouts takes ~1 ms or less: ten times the steps by default, so that
+    # the timing covers a steady clock as the 720p one does
+    short = w.name in ("share32", "image_anchor")
+    if args.steps is None:
+        args.steps = 100 if short else 10
+    if args.warmup is None:
+        args.warmup = 20 if short else 2
     if w.mode == "wdelta":
         print(json.dumps(run_trajectory(args, w)), flush=True)
         return 0
