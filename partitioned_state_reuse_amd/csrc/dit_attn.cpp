@@ -187,7 +187,7 @@ int make_tail(const AttnDesc &desc, const uint8_t *recompute, int B, int S_q, in
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return DIT_ERR_HIP;
   const int64_t slots = std::max<int64_t>(1, (int64_t)cus * dit::kMinBlocks);
-  const int64_t rpw = 256 / (D / 8);
+  const int64_t rpw = (int64_t)dit::kWaves * 64 / (D / 8);  // row-heads per pass of a tail workgroup
   const int64_t passes = ((int64_t)B * S_q * H + rpw - 1) / rpw;
   const int64_t chunk_passes = std::min<int64_t>(16, std::max<int64_t>(1, passes / (8 * slots)));
   const int64_t n_chunks = (passes + chunk_passes - 1) / chunk_passes;

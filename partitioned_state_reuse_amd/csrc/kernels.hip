@@ -1,5 +1,7 @@
-// HIP kernels for gfx950 (CDNA4): partition attention with state-cache update, state merge,
-// partition importance, and the local-change reduction.
+// HIP kernels for gfx950 (CDNA4): partition attention with state-cache update (optionally
+// with the reused states' pre-merge in the same launch), state merge (all planes, selected
+// planes plus a partial state, fp8 codes), partition importance, and the local-change
+// reduction.
 //
 // The operation follows "DiTango: Cost-Effective Parallel Diffusion Generation with
 // Selective Attention State Reuse" (technical summary, "Methodology §2, State Composition"
@@ -1082,9 +1084,8 @@ template <int D>
 __device__ __forceinline__ void premerge_chunks(const u16 *__restrict__ cache_o, const float *__restrict__ cache_lse,
                                                 const AttnDesc &desc, const TailMerge &tm) {
   constexpr int TPR = D / 8;
-  constexpr int RPW = 256 / TPR;  // row-heads per pass of the workgroup
+  constexpr int RPW = kWaves * 64 / TPR;  // row-heads per pass of the workgroup
   constexpr int PMAX = DIT_MAX_PARTITIONS;
-  static_assert(kWaves * 64 == 256, "the pre-merge takes 256 threads per workgroup");
   __shared__ float wts_all[RPW][PMAX + 1];
   __shared__ uint32_t claimed;
   const int S_q = desc.S_q, H = desc.H;
