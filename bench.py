@@ -77,9 +77,9 @@ def measured_counters(workload: str, kernel: str) -> dict:
 
 
 def measured_power(workload: str) -> dict:
-    """Steady-state socket power and graphics clock of the attention kernel and of the merge
-    from the committed power trace of this workload (bench.py --power-trace); empty when the
-    kernel sources changed since it was taken."""
+    """Steady-state socket power and graphics clock of the attention kernel, of the merge and of
+    the whole step (one call, plain sequence) from the committed power trace of this workload
+    (bench.py --power-trace); empty when the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"power_{workload}.txt")
     if not os.path.exists(path):
         return {}
@@ -88,7 +88,7 @@ def measured_power(workload: str) -> dict:
     if not m or m.group(1) != kernel_source_sha256():
         return {}
     out = {"source": f"profiles/power_{workload}.txt"}
-    for name in ("attention", "merge"):
+    for name in ("attention", "merge", "one_call", "plain_step"):
         r = re.search(rf"^# {name} steady state \((\d+) samples\): socket power (\d+) W, gfx clock per XCD ([\d ]+) MHz "
                       rf"\(mean (\d+)\)", text, flags=re.M)
         if r:
@@ -753,8 +753,11 @@ def layer_extras(w: W.Workload, args, dev, ctx) -> dict:
 def power_trace(w: W.Workload) -> str:
     """Socket power, per-XCD graphics clock and temperatures (amd-smi, sampled about every
     0.3 s by a child process) while the selective step's attention kernel runs back to back
-    for 10 s, then the merge for 6 s, with idle gaps between: whether a kernel runs at the
-    clock ceiling or the power ceiling."""
+    for 10 s, then the merge for 6 s, then the whole step for 8 s each way (the library's one
+    call, with the reused states merged inside the attention launch, and the plain sequence of
+    attention, merge of all states and local-change finish), with idle gaps between: whether a
+    kernel runs at the clock ceiling or the power ceiling, and what the in-launch merge does to
+    the power and clock of the step."""
     import subprocess
     import threading
     import torch
@@ -815,11 +818,30 @@ def power_trace(w: W.Workload) -> str:
     time.sleep(3)
     mer_ms = run_for("merge", 6, lambda: api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream), 50)
     phase[0] = "idle"
+    time.sleep(3)
+
+    def one_call():
+        api.attn_partitioned(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse, sa.out, sa.lse,
+                             local_part=w.local_part, cache_valid=valid, delta_out=sa.delta, workspace=sa.workspace,
+                             stream=stream)
+
+    def plain():
+        api.partition_attention(q, k, v, w.q_offsets, w.kv_offsets, mask, sa.cache_o, sa.cache_lse,
+                                local_part=w.local_part, cache_valid=valid, workspace=sa.workspace, stream=stream)
+        api.state_merge(sa.cache_o, sa.cache_lse, sa.out, sa.lse, stream=stream)
+        api.local_change_finalize(sa.workspace, 1, w.S_q, w.H, w.D, w.q_offsets, sa.delta, stream=stream)
+
+    one_ms = run_for("one_call", 8, one_call, 5)
+    phase[0] = "idle"
+    time.sleep(3)
+    pl_ms = run_for("plain_step", 8, plain, 5)
+    phase[0] = "idle"
     time.sleep(2)
     done.set()
     th.join()
     lines = [f"# source_sha256 {kernel_source_sha256()}",
-             f"# {w.name}: attention kernel {att_ms:.2f} ms per launch back to back, merge {mer_ms:.3f} ms",
+             f"# {w.name}: attention kernel {att_ms:.2f} ms per launch back to back, merge {mer_ms:.3f} ms, "
+             f"step {one_ms:.3f} ms as one call, {pl_ms:.3f} ms as the plain sequence",
              "# time_s  phase       socket_W  gfx_MHz per XCD                                  hotspot_C mem_C"]
     t_first = samples[0][0] if samples else 0.0
     prev = None
@@ -829,7 +851,7 @@ def power_trace(w: W.Workload) -> str:
         prev = (ph, pw, clk, hot, mem)
         lines.append(f"{t - t_first:7.2f}  {ph:<10} {str(pw):>8}  {' '.join(f'{c:>5}' for c in clk):<48} {str(hot):>8} {str(mem):>5}")
     # the sampler refreshes about once a second; steady state: samples at least 1.5 s into a phase
-    for name in ("attention", "merge"):
+    for name in ("attention", "merge", "one_call", "plain_step"):
         t_start = min((t for t, ph, *_ in samples if ph == name), default=None)
         sel = [s for s in samples if s[1] == name and t_start is not None and s[0] - t_start >= 1.5 and s[2] is not None]
         if sel:
