@@ -419,6 +419,13 @@ class SelectiveAttention:
             raise DitError(-7, f"{what} needs the bf16 state cache")
 
     def step(self, q, k, v, recompute, *, want_importance=False, want_delta=False, scale=0.0, stream=None):
+        """One selective step: the states of the (block, partition) pairs flagged in
+        `recompute` are computed and written into the cache, the others are reused, and every
+        block's states are merged into `out` / `lse`.  `want_importance` (anchor steps) fills
+        `importance`; `want_delta` fills `delta` with the local-state change when every local
+        slot already holds a state.  Returns whether `delta` was computed.  With the bf16 cache,
+        a step that reuses states and asks for no importance merges the reused states inside
+        the attention launch."""
         recompute = np.asarray(recompute, dtype=np.uint8).reshape(self.n_qb, self.P)
         local_valid = all(self.valid[i, self.local_part[i]] for i in range(self.n_qb))
         do_delta = want_delta and local_valid
