@@ -18,6 +18,8 @@ MODES = {"wdelta": DIT_PLAN_WDELTA, "distance": DIT_PLAN_DISTANCE, "anchor": DIT
 
 
 class DitError(RuntimeError):
+    """A library call returned a non-zero status; `code` is the DIT_ERR_* value."""
+
     def __init__(self, code: int, message: str):
         super().__init__(f"{message} (status {code})")
         self.code = code
@@ -29,6 +31,7 @@ def _check(code: int) -> None:
 
 
 def status_string(code: int) -> str:
+    """dit_status_string: the name of a status code."""
     return _lib.lib().dit_status_string(code).decode()
 
 
@@ -92,6 +95,8 @@ def _ws(t: Optional[torch.Tensor], name: str) -> Tuple[Optional[int], int]:
 
 
 def workspace_bytes(B: int, S_q: int, H: int, D: int, n_qb: int, P: int) -> int:
+    """dit_attn_workspace_bytes: device workspace bytes a step of these sizes needs (0 if the
+    sizes are invalid)."""
     return int(_lib.lib().dit_attn_workspace_bytes(B, S_q, H, D, n_qb, P))
 
 
@@ -240,6 +245,8 @@ def state_compose(cache_o, cache_lse, group_offsets, out_o, out_lse, *, stream=N
 
 
 def importance(cache_lse, lse, q_offsets, importance_out, *, stream=None) -> None:
+    """dit_importance: the partition importance [B, n_qb, P] from the cached lse planes and the
+    merged lse, in a second pass (no workspace)."""
     P, B, S_q, H = cache_lse.shape
     n_qb = len(q_offsets) - 1
     _check(_lib.lib().dit_importance(
@@ -248,6 +255,8 @@ def importance(cache_lse, lse, q_offsets, importance_out, *, stream=None) -> Non
 
 
 def local_change_finalize(workspace, B, S_q, H, D, q_offsets, delta_out, *, stream=None) -> None:
+    """dit_local_change_finalize: the local-state change [B, n_qb] from the partial sums the
+    attention kernel left in the workspace."""
     wp, ws_bytes = _ws(workspace, "workspace")
     n_qb = len(q_offsets) - 1
     _check(_lib.lib().dit_local_change_finalize(wp, ws_bytes, B, S_q, H, D, _i32(q_offsets), n_qb,
@@ -267,6 +276,8 @@ class Planner:
         self._h = h
 
     def next(self, step: int) -> Tuple[np.ndarray, List[List[int]]]:
+        """The recompute mask [n_qb, P] of `step` and each block's chosen groups (local group
+        first)."""
         mask = (ctypes.c_uint8 * (self.n_qb * self.P))()
         groups = (ctypes.c_int32 * (self.n_qb * self.G))()
         _check(_lib.lib().dit_planner_next(self._h, int(step), mask, groups))
@@ -275,6 +286,8 @@ class Planner:
         return m, [[int(x) for x in row if x >= 0] for row in g]
 
     def observe(self, step: int, importance=None, delta=None) -> None:
+        """Feed the step's measurements: importance [n_qb, P] (anchor steps) and/or the local
+        change [n_qb]."""
         def f32(a):
             if a is None:
                 return None
@@ -283,11 +296,13 @@ class Planner:
         _check(_lib.lib().dit_planner_observe(self._h, int(step), f32(importance), f32(delta)))
 
     def scores(self, step: int) -> np.ndarray:
+        """The predicted reuse error [n_qb, G] that next(step) would rank the groups by."""
         out = (ctypes.c_double * (self.n_qb * self.G))()
         _check(_lib.lib().dit_planner_scores(self._h, int(step), out))
         return np.frombuffer(out, dtype=np.float64).reshape(self.n_qb, self.G).copy()
 
     def close(self) -> None:
+        """Release the native planner (also done on garbage collection)."""
         if getattr(self, "_h", None) is not None and self._h.value:
             _lib.lib().dit_planner_destroy(self._h)
             self._h = ctypes.c_void_p()
