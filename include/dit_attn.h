@@ -35,10 +35,10 @@
  *                                              row-heads reads one contiguous range)
  *       out          [B, S_q, H, D] bf16       merged output
  *       lse          [B, H, S_q] f32           merged lse
- *     All device buffers must be 16-byte aligned.  Buffers a call writes (out, lse, the
- *     cache, importance_out, delta_out, the workspace) must not overlap each other or the
- *     buffers it reads, except where a call says otherwise (dit_state_merge_masked may take
- *     its extra state in out / lse itself).
+ *     All device buffers must be 16-byte aligned.  q, k, v, the cache, out, lse,
+ *     importance_out, delta_out and the workspace must not overlap one another (a call
+ *     writes the cache slots it recomputes and reads the others), except where a call says
+ *     otherwise (dit_state_merge_masked may take its extra state in out / lse itself).
  *   - q_offsets [n_qb+1]: query-block offsets, q_offsets[0] = 0, strictly increasing,
  *     q_offsets[n_qb] = S_q.  kv_offsets [P+1]: partition offsets, kv_offsets[0] = 0,
  *     non-decreasing (empty partitions allowed), kv_offsets[P] = S_kv.
