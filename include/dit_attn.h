@@ -35,9 +35,9 @@
  *                                              row-heads reads one contiguous range)
  *       out          [B, S_q, H, D] bf16       merged output
  *       lse          [B, H, S_q] f32           merged lse
- *     All device buffers must be 16-byte aligned.  q, k, v, the cache, out, lse,
- *     importance_out, delta_out and the workspace must not overlap one another (a call
- *     writes the cache slots it recomputes and reads the others), except where a call says
+ *     All device buffers must be 16-byte aligned.  The buffers a call may write (the cache,
+ *     out, lse, importance_out, delta_out, the workspace) must not overlap one another or
+ *     q, k, v (the read-only inputs may overlap each other), except where a call says
  *     otherwise (dit_state_merge_masked may take its extra state in out / lse itself).
  *   - q_offsets [n_qb+1]: query-block offsets, q_offsets[0] = 0, strictly increasing,
  *     q_offsets[n_qb] = S_q.  kv_offsets [P+1]: partition offsets, kv_offsets[0] = 0,
