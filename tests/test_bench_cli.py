@@ -42,3 +42,22 @@ def test_counter_record_follows_the_same_source_hash():
         assert 0.5 < got["clock_ghz_under_load"] <= 2.4
         assert 0.0 < got["mfma_busy_frac"] <= 1.0
         assert abs(got["peak_tflops_at_that_clock"] - 2500.0 * got["clock_ghz_under_load"] / 2.4) < 1.0
+
+
+def test_power_record_follows_the_same_source_hash(monkeypatch):
+    """The committed power trace is parsed (attention, merge and both step phases) while its
+    source hash matches the kernel sources, and ignored once it does not."""
+    sys.path.insert(0, ROOT)
+    import bench
+    text = open(os.path.join(ROOT, "profiles", "power_video720p.txt")).read()
+    got = bench.measured_power("video720p")
+    if f"# source_sha256 {bench.kernel_source_sha256()}" in text:
+        for phase in ("attention", "merge", "one_call", "plain_step"):
+            assert 500 < got[phase]["socket_w"] < 2000
+            assert len(got[phase]["gfx_mhz_per_xcd"]) == 8
+            assert min(got[phase]["gfx_mhz_per_xcd"]) <= got[phase]["gfx_mhz_mean"] <= max(got[phase]["gfx_mhz_per_xcd"])
+    else:
+        assert got == {}
+    # once the kernel sources differ from those the trace was taken on, it is not used
+    monkeypatch.setattr(bench, "kernel_source_sha256", lambda: "0" * 64)
+    assert bench.measured_power("video720p") == {}
